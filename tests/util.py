@@ -1,0 +1,80 @@
+"""Test-side helpers: bit-pattern decoding, the tolerance rule and rounding checks.
+
+These helpers hold no arithmetic of the forward path; they only read bit
+patterns and compare numbers.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+REL_TOL = 8e-3
+ABS_TOL = 1e-3
+
+
+def bf16_value(bits) -> np.ndarray:
+    """float64 value of bf16 bit patterns (test-side decode, independent of the oracle's)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+    return np.frombuffer((b << 16).astype(np.uint32).tobytes(), dtype=np.float32).reshape(b.shape).astype(np.float64)
+
+
+def bf16_neighbours(bits):
+    """Values of the next bf16 below and above each finite pattern."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    neg = (b & 0x8000) != 0
+    mag = b & 0x7FFF
+    zero = mag == 0
+    # positive y: one pattern up / down.  negative y: magnitude down is the
+    # larger value.  zero (either sign): the smallest subnormals of each sign.
+    hi = np.where(neg, (mag - 1) | 0x8000, mag + 1)
+    lo = np.where(neg, (mag + 1) | 0x8000, mag - 1)
+    hi = np.where(zero, 0x0001, hi)
+    lo = np.where(zero, 0x8001, lo)
+    return bf16_value(lo.astype(np.uint16)), bf16_value(hi.astype(np.uint16))
+
+
+def assert_correctly_rounded(bits, exact, rel_slack: float = 1e-12, abs_slack: float = 0.0):
+    """Assert each bf16 pattern is a nearest bf16 to ``exact`` (float64 reference).
+
+    Checked against both neighbours in bit-pattern space, so it does not rely
+    on any particular rounding routine.  ``rel_slack`` absorbs the ~1e-16
+    difference between two float64 evaluations of the same expression.
+    """
+    bits = np.asarray(bits, dtype=np.uint16)
+    exact = np.asarray(exact, dtype=np.float64)
+    y = bf16_value(bits)
+    lo, hi = bf16_neighbours(bits)
+    err = np.abs(y - exact)
+    slack = rel_slack * np.abs(exact) + abs_slack
+    ok = (err <= np.abs(lo - exact) + slack) & (err <= np.abs(hi - exact) + slack)
+    if not ok.all():
+        idx = np.argwhere(~ok)[0]
+        raise AssertionError(
+            f"{(~ok).sum()} of {ok.size} not correctly rounded; first at {tuple(idx)}: "
+            f"bits={bits[tuple(idx)]:#06x} value={y[tuple(idx)]!r} exact={exact[tuple(idx)]!r}")
+
+
+def tolerance_report(gpu_bits, ref_bits, rel: float = REL_TOL, abs_: float = ABS_TOL):
+    """Per-element rule |gpu - ref| <= rel*|ref| + abs; any NaN/Inf in either fails."""
+    g = bf16_value(gpu_bits)
+    r = bf16_value(ref_bits)
+    finite = np.isfinite(g) & np.isfinite(r)
+    err = np.abs(g - r)
+    bound = rel * np.abs(r) + abs_
+    bad = ~finite | (err > bound)
+    rep = {
+        "n": int(g.size),
+        "violations": int(bad.sum()),
+        "max_abs": float(np.max(np.where(finite, err, 0.0))) if g.size else 0.0,
+        "max_rel": float(np.max(np.where(finite, err / np.maximum(np.abs(r), 1e-30), 0.0))) if g.size else 0.0,
+        "bitwise_equal": int((np.asarray(gpu_bits) == np.asarray(ref_bits)).sum()),
+    }
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        rep["first"] = {"index": i, "gpu": float(g[i]), "ref": float(r[i])}
+    return rep
+
+
+def assert_within_tolerance(gpu_bits, ref_bits, what: str = ""):
+    rep = tolerance_report(gpu_bits, ref_bits)
+    assert rep["violations"] == 0, f"{what}: {rep}"
+    return rep
