@@ -1,0 +1,255 @@
+/*
+ * bi.h -- batch-invariant transformer forward kernels for AMD MI355X (gfx950).
+ *
+ * What the library computes.  "Deterministic and bit-exact inference" (M-0002
+ * record, field `technical`, the Invariance route, and its body section "How
+ * it works") describes kernels that fix the reduction order of every output
+ * element whatever the batch size, for RMSNorm, matrix multiplication and
+ * attention -- the last with a fixed split *size* along the key/value axis
+ * instead of a fixed number of splits.  The "Receipts" page (opening
+ * paragraph) asks for outputs that do not depend on other requests in the
+ * batch, on the prompt cache or on run-ahead, i.e. on chunked prefill; its
+ * section "What a receipt proves" adds that bits are promised within one
+ * device class and one build, and that parallel workers split rows, never
+ * sums.  The M-0002 threat model ("No atomic functions") and its
+ * "Residual nondeterminism" limitation rule out atomics, including in integer
+ * de-quantisation.
+ *
+ * Contract of every entry point below.  With one build of this library on
+ * gfx950, output row r depends only on row r's own inputs (for attention: on
+ * the request's own keys/values and absolute positions).  It never depends on
+ * the number of rows M, the batch size B, the row's position in the batch,
+ * chunk boundaries of a prefill, KV-cache capacity, other requests, or on the
+ * run.  No kernel uses atomic instructions, split-K or stream-K.
+ *
+ * Conventions.
+ *  - bf16 / fp16 tensors are passed as raw 16-bit patterns (bi_bf16, bi_f16).
+ *  - All tensors are row-major and dense (last index contiguous) in device
+ *    memory, except where an argument is marked "host".
+ *  - Device pointers must be 16-byte aligned; row lengths that are given in
+ *    elements must keep every row 16-byte aligned where stated.
+ *  - Accumulation is fp32; every bf16 output is rounded to nearest even.
+ *  - Ownership: the caller allocates and owns every buffer (inputs, outputs,
+ *    KV pools, workspaces).  The library allocates nothing and keeps no
+ *    mutable global state; calls are reentrant and asynchronous on the given
+ *    stream (0 = the null stream).  No call synchronises the device.
+ *  - Errors: every argument check runs before anything is launched.  On an
+ *    error the call returns a non-BI_OK status, launches nothing and leaves
+ *    every output untouched.  A failed launch returns BI_ERR_HIP.  No C++
+ *    exception crosses this interface.
+ */
+#ifndef BI_H_
+#define BI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t bi_bf16; /* raw bfloat16 bits */
+typedef uint16_t bi_f16;  /* raw IEEE binary16 bits */
+
+typedef enum {
+  BI_OK = 0,
+  BI_ERR_NULL = 1,        /* a required pointer is NULL */
+  BI_ERR_SHAPE = 2,       /* a size is zero, negative or inconsistent */
+  BI_ERR_UNSUPPORTED = 3, /* a size outside what the kernels implement */
+  BI_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  BI_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required */
+  BI_ERR_HIP = 6          /* the HIP runtime reported a launch error */
+} bi_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* bi_status_str(bi_status status);
+
+/* Identifier of this build: 16 hex digits hashing the kernel sources and the
+ * compiler flags.  Bits are promised only between calls of the same build on
+ * the same device class ("Receipts", "What a receipt proves"). */
+const char* bi_build_id(void);
+
+/* The fixed key/value split size of decode attention: 256 keys. */
+int bi_kv_split_size(void);
+
+/* Compile-time tile shape of bi_gemm / bi_gemm_w4 (the same for every M):
+ * writes BM, BN, BK into out[0..2]. */
+void bi_gemm_tile(int out[3]);
+
+/* ------------------------------------------------------------------ RMSNorm
+ * y[r, j] = bf16( x[r, j] * rsqrt(sum_j x[r, j]^2 / hidden + eps) * gamma[j] )
+ * (the RMSNorm of M-0002 `technical`).  One fixed fp32 reduction tree per row,
+ * chosen from `hidden` alone.
+ *   x     [rows, hidden] bf16      y [rows, hidden] bf16 (may not alias x)
+ *   gamma [hidden] bf16
+ *   rows >= 1; hidden % 8 == 0, 8 <= hidden <= 16384; eps finite, >= 0.     */
+bi_status bi_rmsnorm(const bi_bf16* x, const bi_bf16* gamma, bi_bf16* y,
+                     int64_t rows, int64_t hidden, float eps, hipStream_t stream);
+
+/* --------------------------------------------------------------------- GEMM
+ * C = A * W^T, fp32 accumulation, bf16 output (M-0002 `technical`: matrix
+ * multiplication).  One tile shape for every M (see bi_gemm_tile), no
+ * split-K: each C[i, j] is accumulated over k = 0..K-1 in the same order for
+ * every M and every position of row i.
+ *   A [M, K] bf16   W [N, K] bf16   C [M, N] bf16 (must not alias A or W)
+ *   M >= 1; N >= 8, N % 8 == 0; K >= 64, K % 64 == 0.                        */
+bi_status bi_gemm(const bi_bf16* A, const bi_bf16* W, bi_bf16* C,
+                  int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* C = A * Wd^T with Wd de-quantised inside the kernel from symmetric int4:
+ * Wd[j, k] = bf16(code[j, k] * Ws[j, k / 32]) where code[j, k] is the
+ * two's-complement nibble (range -8..7) of byte Wq[j, k / 2], low nibble for
+ * even k, high nibble for odd k.  De-quantisation is elementwise with no
+ * atomics ("Residual nondeterminism" in the M-0002 limitations).  The result
+ * is bit-identical to bi_gemm on the de-quantised weight.
+ *   A [M, K] bf16   Wq [N, K/2] u8   Ws [N, K/32] fp16   C [M, N] bf16
+ *   same size rules as bi_gemm.                                              */
+bi_status bi_gemm_w4(const bi_bf16* A, const uint8_t* Wq, const bi_f16* Ws, bi_bf16* C,
+                     int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/* --------------------------------------------------------- elementwise steps
+ * h[i] = bf16(x[i] + o[i]) for i < n (the residual connection).  n % 8 == 0.
+ * h may alias x or o.                                                        */
+bi_status bi_add(const bi_bf16* x, const bi_bf16* o, bi_bf16* h, int64_t n, hipStream_t stream);
+
+/* act[r, j] = bf16(silu(g) * u), g = gu[r, j], u = gu[r, F + j], silu(g) =
+ * g / (1 + exp(-g)).  gu [rows, 2F] bf16 (gate columns then up columns),
+ * act [rows, F] bf16.  rows >= 1, F % 8 == 0.                               */
+bi_status bi_swiglu(const bi_bf16* gu, bi_bf16* act, int64_t rows, int64_t F, hipStream_t stream);
+
+/* --------------------------------------------------------- RoPE + KV append
+ * For each token row r of qkv [rows, (Hq + 2 Hkv) * D] (query heads, then key
+ * heads, then value heads, D contiguous per head):
+ *   q_out[r, h, :] = RoPE(q[r, h, :], pos[r])            (h < Hq)
+ *   k_pool[kv_row[r], g, :] = RoPE(k[r, g, :], pos[r])   (g < Hkv)
+ *   v_pool[kv_row[r], g, :] = v[r, g, :]
+ * RoPE rotates the pair (i, i + D/2), i < D/2, by pos * theta^(-2 i / D),
+ * computed from the absolute position (so a prompt's keys do not depend on
+ * how it was chunked: "Receipts", opening paragraph).  theta == 0 disables
+ * the rotation (plain copy).
+ *   pos [rows] int32 device, >= 0;  kv_row [rows] int64 device, row index
+ *   into the pools k_pool, v_pool [*, Hkv, D] bf16.  D in {64, 128};
+ *   Hq % Hkv == 0.                                                          */
+bi_status bi_rope_kv(const bi_bf16* qkv, const int32_t* pos, const int64_t* kv_row,
+                     bi_bf16* q_out, bi_bf16* k_pool, bi_bf16* v_pool,
+                     int64_t rows, int Hq, int Hkv, int D, double theta, hipStream_t stream);
+
+/* ------------------------------------------------------- prefill attention
+ * Causal attention of one sequence's chunk of T queries at absolute
+ * positions q_start .. q_start + T - 1 over that sequence's cache:
+ *   o[t, h, :] = bf16( sum_{s <= q_start + t} softmax_s(scale q[t,h,:].k[s,g,:]) v[s,g,:] )
+ * with g = h / (Hq / Hkv).  Key blocks and query tiles are aligned to
+ * absolute position 0, so every query visits the same key blocks in the same
+ * order whatever the chunking ("Receipts", opening paragraph: independent of
+ * the prompt cache and run-ahead).
+ *   q [T, Hq * D] bf16; k_cache, v_cache [>= q_start + T, Hkv, D] bf16 with
+ *   keys 0 .. q_start + T - 1 valid; o [T, Hq * D] bf16.
+ *   T >= 1, q_start >= 0; D in {64, 128}; Hq / Hkv in {1, 2, 4}.             */
+bi_status bi_attn_prefill(const bi_bf16* q, const bi_bf16* k_cache, const bi_bf16* v_cache,
+                          bi_bf16* o, int64_t q_start, int64_t T,
+                          int Hq, int Hkv, int D, float scale, hipStream_t stream);
+
+/* -------------------------------------------------------- decode attention
+ * One query per request b over its L_b cached keys (the newest at position
+ * L_b - 1), split into fixed 256-key units (M-0002 `technical`: a fixed split
+ * size, not a fixed number of splits).  Unit s covers keys [256 s,
+ * min(256 s + 256, L_b)); its (max, sum, weighted values) go to the workspace
+ * in fp32, and a second kernel merges the units of each request in
+ * ascending s.
+ *   q [B, Hq * D] bf16; k_all, v_all [sum L, Hkv, D] bf16 packed;
+ *   kv_offset [B] int64 device: first row of request b in k_all / v_all;
+ *   kv_len [B] int32 device: L_b, 1 <= L_b <= max_kv_len (a request outside
+ *   that range gets NaN output, as the device cannot return an error);
+ *   B >= 1 and max_kv_len >= 1 are host values used only to size the grid;
+ *   D in {64, 128}; Hq / Hkv in {1, 2, 4, 8}; o [B, Hq * D] bf16.
+ *   ws: device workspace of at least bi_attn_decode_workspace() bytes.       */
+size_t bi_attn_decode_workspace(int B, int64_t max_kv_len, int Hq, int D);
+bi_status bi_attn_decode(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* v_all,
+                         const int64_t* kv_offset, const int32_t* kv_len,
+                         int B, int64_t max_kv_len, int Hq, int Hkv, int D, float scale,
+                         void* ws, size_t ws_bytes, bi_bf16* o, hipStream_t stream);
+
+/* ------------------------------------------------------------ decoder block
+ * One forward step of a pre-norm decoder block over a batch of sequences:
+ *   n1 = RMSNorm(x, gamma1); qkv = n1 Wqkv^T; q, k = RoPE(q, k); append k, v;
+ *   a = Attn(q, cache); o = a Wo^T; h = x + o;
+ *   [FFN] n2 = RMSNorm(h, gamma2); gu = n2 Wgu^T; act = silu(g) u;
+ *         d = act Wdown^T; y = h + d      (without FFN, y = h)
+ * with a bf16 rounding at every arrow.  Sequences with q_len == 1 use decode
+ * attention; longer ones use prefill attention.                             */
+typedef enum { BI_WEIGHTS_BF16 = 0, BI_WEIGHTS_INT4_G32 = 1 } bi_weight_format;
+
+typedef struct {
+  int hidden;        /* H, % 8 == 0 */
+  int n_q_heads;     /* Hq */
+  int n_kv_heads;    /* Hkv, Hq / Hkv in {1, 2, 4} */
+  int head_dim;      /* D in {64, 128} */
+  int ffn;           /* F (% 64 == 0), or 0 for a block without FFN */
+  float eps;         /* RMSNorm epsilon */
+  double rope_theta; /* 0 = no rotary embedding */
+  int weight_format; /* bi_weight_format */
+} bi_block_cfg;
+
+typedef struct {
+  const void* w;       /* bf16 [N, K], or int4 packed u8 [N, K/2] */
+  const bi_f16* scale; /* int4 only: fp16 [N, K/32]; NULL for bf16 */
+} bi_weight;
+
+typedef struct {
+  const bi_bf16* gamma1; /* [H] */
+  const bi_bf16* gamma2; /* [H] (FFN only) */
+  bi_weight qkv;         /* N = (Hq + 2 Hkv) D, K = H; rows: q heads, k heads, v heads */
+  bi_weight o;           /* N = H, K = Hq D */
+  bi_weight gate_up;     /* N = 2F, K = H; rows 0..F-1 gate, F..2F-1 up (FFN only) */
+  bi_weight down;        /* N = H, K = F (FFN only) */
+} bi_block_weights;
+
+typedef struct {
+  int32_t q_len;   /* new tokens of this sequence in the step (>= 1) */
+  int32_t ctx_len; /* tokens already in its cache (>= 0) */
+  int64_t kv_base; /* pool row holding its position 0 */
+} bi_seq;
+
+typedef struct {
+  bi_bf16* k;       /* [rows, Hkv, D] */
+  bi_bf16* v;       /* [rows, Hkv, D] */
+  int64_t rows;     /* capacity of the pools in token rows */
+} bi_kv_pool;
+
+/* Step metadata.  The kernels read a packed device copy of the step
+ * description; bi_step_pack writes it into caller host memory, and the caller
+ * uploads those bytes to device memory (e.g. through pinned memory) and
+ * passes the device address to bi_block_forward together with the same host
+ * bi_seq array.  This keeps every call free of hidden synchronisation.      */
+size_t bi_step_meta_bytes(int n_seqs, int64_t n_tokens);
+bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t bytes);
+
+/* Offsets (bytes into the block workspace) of every intermediate stage, for
+ * inspection after a call: each is bf16 row-major [M, width].  Entries of a
+ * stage the block does not have (no FFN) are SIZE_MAX.                      */
+typedef struct {
+  size_t n1, qkv, q, attn, o, h, n2, gu, act, d;
+  size_t decode_partials;
+  size_t total;
+} bi_block_ws_layout;
+
+bi_status bi_block_workspace(const bi_block_cfg* cfg, const bi_seq* seqs, int n_seqs,
+                             bi_block_ws_layout* layout);
+
+/*   seqs / n_seqs: host description of the step (>= 1 sequence); rows of x
+ *     and y are the sequences' new tokens concatenated in order (M = sum of
+ *     q_len).  d_meta: device copy of bi_step_pack(seqs) output.
+ *   kv: pools updated in place at rows kv_base + ctx_len .. + q_len - 1;
+ *     rows kv_base .. kv_base + ctx_len - 1 must hold the cached keys/values.
+ *   x, y [M, H] bf16 (y may not alias x).  ws: >= layout.total bytes.       */
+bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w,
+                           const bi_seq* seqs, int n_seqs, const void* d_meta,
+                           const bi_kv_pool* kv, const bi_bf16* x, bi_bf16* y,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H_ */

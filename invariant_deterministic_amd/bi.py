@@ -1,0 +1,348 @@
+"""ctypes binding of libbi.so (argument marshalling only).
+
+Every computation runs in the library's HIP kernels; this module only checks
+tensor dtypes/devices, passes raw device pointers and the current HIP stream,
+and turns error codes into exceptions.  PyTorch supplies device memory and
+streams.  There is no fallback: if libbi.so is missing or fails to load, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbi.so")
+
+BI_WEIGHTS_BF16 = 0
+BI_WEIGHTS_INT4_G32 = 1
+
+c_void_p = ctypes.c_void_p
+c_int = ctypes.c_int
+c_int64 = ctypes.c_int64
+c_size_t = ctypes.c_size_t
+c_float = ctypes.c_float
+c_double = ctypes.c_double
+
+
+class BiError(RuntimeError):
+    pass
+
+
+class bi_block_cfg(ctypes.Structure):
+    _fields_ = [("hidden", c_int), ("n_q_heads", c_int), ("n_kv_heads", c_int), ("head_dim", c_int),
+                ("ffn", c_int), ("eps", c_float), ("rope_theta", c_double), ("weight_format", c_int)]
+
+
+class bi_weight(ctypes.Structure):
+    _fields_ = [("w", c_void_p), ("scale", c_void_p)]
+
+
+class bi_block_weights(ctypes.Structure):
+    _fields_ = [("gamma1", c_void_p), ("gamma2", c_void_p), ("qkv", bi_weight), ("o", bi_weight),
+                ("gate_up", bi_weight), ("down", bi_weight)]
+
+
+class bi_seq(ctypes.Structure):
+    _fields_ = [("q_len", ctypes.c_int32), ("ctx_len", ctypes.c_int32), ("kv_base", ctypes.c_int64)]
+
+
+class bi_kv_pool(ctypes.Structure):
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("rows", c_int64)]
+
+
+class bi_block_ws_layout(ctypes.Structure):
+    _fields_ = [(n, c_size_t) for n in ("n1", "qkv", "q", "attn", "o", "h", "n2", "gu", "act", "d",
+                                        "decode_partials", "total")]
+
+
+# name -> (restype, argtypes), mirroring include/bi.h
+_SIGNATURES = {
+    "bi_status_str": (ctypes.c_char_p, [c_int]),
+    "bi_build_id": (ctypes.c_char_p, []),
+    "bi_kv_split_size": (c_int, []),
+    "bi_gemm_tile": (None, [ctypes.POINTER(c_int)]),
+    "bi_rmsnorm": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_float, c_void_p]),
+    "bi_gemm": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
+    "bi_gemm_w4": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
+    "bi_add": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p]),
+    "bi_swiglu": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p]),
+    "bi_rope_kv": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int,
+                           c_int, c_int, c_double, c_void_p]),
+    "bi_attn_prefill": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int, c_int,
+                                c_int, c_float, c_void_p]),
+    "bi_attn_decode_workspace": (c_size_t, [c_int, c_int64, c_int, c_int]),
+    "bi_attn_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int,
+                               c_int, c_int, c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "bi_step_meta_bytes": (c_size_t, [c_int, c_int64]),
+    "bi_step_pack": (c_int, [ctypes.POINTER(bi_seq), c_int, c_void_p, c_size_t]),
+    "bi_block_workspace": (c_int, [ctypes.POINTER(bi_block_cfg), ctypes.POINTER(bi_seq), c_int,
+                                   ctypes.POINTER(bi_block_ws_layout)]),
+    "bi_block_forward": (c_int, [ctypes.POINTER(bi_block_cfg), ctypes.POINTER(bi_block_weights),
+                                 ctypes.POINTER(bi_seq), c_int, c_void_p, ctypes.POINTER(bi_kv_pool),
+                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+}
+
+_lib = None
+
+
+def lib():
+    """Load libbi.so once (raises if it is missing: there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise BiError(f"{LIB_PATH} is not built; run `python -m invariant_deterministic_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGNATURES)
+
+
+def status_str(code: int) -> str:
+    return lib().bi_status_str(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise BiError(f"{what}: {status_str(code)}")
+
+
+def build_id() -> str:
+    return lib().bi_build_id().decode()
+
+
+def kv_split_size() -> int:
+    return lib().bi_kv_split_size()
+
+
+def gemm_tile():
+    arr = (c_int * 3)()
+    lib().bi_gemm_tile(arr)
+    return tuple(arr)
+
+
+def _stream():
+    return c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return c_void_p(t.data_ptr()) if t is not None else c_void_p(0)
+
+
+def _dev(t: torch.Tensor, dtype, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+BF16 = torch.bfloat16
+HALF_BITS = (torch.float16, torch.int16)
+
+
+# ----------------------------------------------------------------- kernels
+def rmsnorm(x, gamma, eps: float, out=None):
+    _dev(x, BF16, "x"); _dev(gamma, BF16, "gamma")
+    rows, hidden = x.shape
+    out = torch.empty_like(x) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_rmsnorm(_ptr(x), _ptr(gamma), _ptr(out), rows, hidden, eps, _stream()), "bi_rmsnorm")
+    return out
+
+
+def gemm(A, W, out=None):
+    _dev(A, BF16, "A"); _dev(W, BF16, "W")
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("K mismatch")
+    out = torch.empty((M, N), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_gemm(_ptr(A), _ptr(W), _ptr(out), M, N, K, _stream()), "bi_gemm")
+    return out
+
+
+def gemm_w4(A, Wq, Ws, out=None):
+    _dev(A, BF16, "A"); _dev(Wq, torch.uint8, "Wq"); _dev(Ws, HALF_BITS, "Ws")
+    M, K = A.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] * 2 != K or Ws.shape != (N, K // 32):
+        raise ValueError("int4 weight shape mismatch")
+    out = torch.empty((M, N), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_gemm_w4(_ptr(A), _ptr(Wq), _ptr(Ws), _ptr(out), M, N, K, _stream()), "bi_gemm_w4")
+    return out
+
+
+def add(x, o, out=None):
+    _dev(x, BF16, "x"); _dev(o, BF16, "o")
+    out = torch.empty_like(x) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_add(_ptr(x), _ptr(o), _ptr(out), x.numel(), _stream()), "bi_add")
+    return out
+
+
+def swiglu(gu, out=None):
+    _dev(gu, BF16, "gu")
+    rows, two_f = gu.shape
+    F = two_f // 2
+    out = torch.empty((rows, F), dtype=BF16, device=gu.device) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_swiglu(_ptr(gu), _ptr(out), rows, F, _stream()), "bi_swiglu")
+    return out
+
+
+def rope_kv(qkv, pos, kv_row, k_pool, v_pool, Hq, Hkv, D, theta, q_out=None):
+    _dev(qkv, BF16, "qkv"); _dev(pos, torch.int32, "pos"); _dev(kv_row, torch.int64, "kv_row")
+    _dev(k_pool, BF16, "k_pool"); _dev(v_pool, BF16, "v_pool")
+    rows = qkv.shape[0]
+    q_out = torch.empty((rows, Hq * D), dtype=BF16, device=qkv.device) if q_out is None else q_out
+    _check(lib().bi_rope_kv(_ptr(qkv), _ptr(pos), _ptr(kv_row), _ptr(q_out), _ptr(k_pool), _ptr(v_pool),
+                            rows, Hq, Hkv, D, float(theta), _stream()), "bi_rope_kv")
+    return q_out
+
+
+def attn_prefill(q, k_cache, v_cache, q_start, Hq, Hkv, D, scale, out=None):
+    _dev(q, BF16, "q"); _dev(k_cache, BF16, "k_cache"); _dev(v_cache, BF16, "v_cache")
+    T = q.shape[0]
+    if k_cache.shape[0] < q_start + T:
+        raise ValueError("cache shorter than q_start + T")
+    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), int(q_start), T,
+                                 Hq, Hkv, D, float(scale), _stream()), "bi_attn_prefill")
+    return out
+
+
+def attn_decode_workspace(B, max_kv_len, Hq, D) -> int:
+    return int(lib().bi_attn_decode_workspace(B, max_kv_len, Hq, D))
+
+
+def attn_decode(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq, Hkv, D, scale, ws=None, out=None):
+    _dev(q, BF16, "q"); _dev(k_all, BF16, "k_all"); _dev(v_all, BF16, "v_all")
+    _dev(kv_offset, torch.int64, "kv_offset"); _dev(kv_len, torch.int32, "kv_len")
+    B = q.shape[0]
+    need = attn_decode_workspace(B, max_kv_len, Hq, D)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_attn_decode(_ptr(q), _ptr(k_all), _ptr(v_all), _ptr(kv_offset), _ptr(kv_len), B,
+                                int(max_kv_len), Hq, Hkv, D, float(scale), _ptr(ws), ws.numel(), _ptr(out),
+                                _stream()), "bi_attn_decode")
+    return out
+
+
+# ------------------------------------------------------------------ block
+@dataclass
+class BlockConfig:
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int = 0
+    eps: float = 1e-6
+    rope_theta: float = 0.0
+    int4: bool = False
+
+    def c(self):
+        return bi_block_cfg(self.hidden, self.n_q_heads, self.n_kv_heads, self.head_dim, self.ffn,
+                            self.eps, float(self.rope_theta),
+                            BI_WEIGHTS_INT4_G32 if self.int4 else BI_WEIGHTS_BF16)
+
+
+def _seq_array(seqs):
+    arr = (bi_seq * len(seqs))()
+    for i, s in enumerate(seqs):
+        arr[i] = bi_seq(int(s["q_len"]), int(s["ctx_len"]), int(s["kv_base"]))
+    return arr
+
+
+def step_meta(seqs, device="cuda"):
+    """Pack a step description on the host and upload it (a device uint8 tensor)."""
+    arr = _seq_array(seqs)
+    n_tok = sum(int(s["q_len"]) for s in seqs)
+    nbytes = lib().bi_step_meta_bytes(len(seqs), n_tok)
+    if nbytes == 0:
+        raise BiError("bi_step_meta_bytes: invalid step")
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=torch.cuda.is_available())
+    _check(lib().bi_step_pack(arr, len(seqs), c_void_p(host.data_ptr()), nbytes), "bi_step_pack")
+    return host.to(device, non_blocking=True), arr
+
+
+def block_workspace(cfg: BlockConfig, seqs):
+    arr = _seq_array(seqs)
+    lay = bi_block_ws_layout()
+    c = cfg.c()
+    _check(lib().bi_block_workspace(ctypes.byref(c), arr, len(seqs), ctypes.byref(lay)), "bi_block_workspace")
+    return lay
+
+
+class Block:
+    """A decoder block whose weights live in device tensors.
+
+    weights: dict with gamma1, gamma2 (bf16 [H]); w_qkv, w_o, w_gate_up, w_down as
+    bf16 [N, K] tensors, or (for int4) (uint8 [N, K/2], fp16-bits [N, K/32]) tuples.
+    """
+
+    def __init__(self, cfg: BlockConfig, weights: dict):
+        self.cfg = cfg
+        self.weights = weights
+        self._c = cfg.c()
+        w = bi_block_weights()
+        w.gamma1 = _ptr(weights["gamma1"])
+        w.gamma2 = _ptr(weights.get("gamma2"))
+        for field, key in (("qkv", "w_qkv"), ("o", "w_o"), ("gate_up", "w_gate_up"), ("down", "w_down")):
+            val = weights.get(key)
+            if val is None:
+                continue
+            if cfg.int4:
+                setattr(w, field, bi_weight(val[0].data_ptr(), val[1].data_ptr()))
+            else:
+                setattr(w, field, bi_weight(val.data_ptr(), None))
+        self._w = w
+
+    def forward(self, x, seqs, k_pool, v_pool, y=None, ws=None, meta=None):
+        """Run one step.  Returns (y, ws, layout); ws holds every intermediate stage."""
+        _dev(x, BF16, "x")
+        if meta is None:
+            meta, arr = step_meta(seqs, x.device)
+        else:
+            arr = _seq_array(seqs)
+        lay = block_workspace(self.cfg, seqs)
+        if ws is None or ws.numel() < lay.total:
+            ws = torch.empty(max(lay.total, 256), dtype=torch.uint8, device=x.device)
+        y = torch.empty_like(x) if y is None else y
+        pool = bi_kv_pool(k_pool.data_ptr(), v_pool.data_ptr(), k_pool.shape[0])
+        _check(lib().bi_block_forward(ctypes.byref(self._c), ctypes.byref(self._w), arr, len(seqs),
+                                      _ptr(meta), ctypes.byref(pool), _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
+                                      _stream()), "bi_block_forward")
+        return y, ws, lay
+
+
+def stage(ws, lay, name, rows, width):
+    """View of one intermediate stage in the block workspace as bf16 [rows, width]."""
+    off = getattr(lay, name)
+    if off == ctypes.c_size_t(-1).value:
+        raise KeyError(f"stage {name} not present")
+    return ws[off:off + rows * width * 2].view(BF16).view(rows, width)
+
+
+# ------------------------------------------------------ host <-> device
+def to_dev(bits: np.ndarray, device="cuda"):
+    """numpy uint16 bf16 bits -> device bf16 tensor."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(BF16).to(device)
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    """device bf16 tensor -> numpy uint16 bits."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)

@@ -1,0 +1,79 @@
+// Device-side helpers shared by the gfx950 kernels of the library.
+//
+// Every kernel in this library follows one rule: the floating-point
+// operations that produce an output element, and their order, are a function
+// of the problem's fixed dimensions (hidden size, N, K, head_dim, heads) and
+// of the element's own absolute coordinates -- never of the number of rows,
+// the batch, a row's position in the batch or a chunk boundary.  No kernel
+// uses atomics.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kWave = 64;
+
+// 16-byte load that streams past the caches (data read exactly once).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// bf16 bits -> fp32 (exact)
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ float bf2f_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf2f_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (hardware v_cvt_pk_bf16_f32 on gfx950)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+}
+
+// Unpack 8 bf16 (one 16-byte chunk) into fp32.
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  f[0] = bf2f_lo(v.x); f[1] = bf2f_hi(v.x);
+  f[2] = bf2f_lo(v.y); f[3] = bf2f_hi(v.y);
+  f[4] = bf2f_lo(v.z); f[5] = bf2f_hi(v.z);
+  f[6] = bf2f_lo(v.w); f[7] = bf2f_hi(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  uint4 r;
+  r.x = pack2bf(f[0], f[1]);
+  r.y = pack2bf(f[2], f[3]);
+  r.z = pack2bf(f[4], f[5]);
+  r.w = pack2bf(f[6], f[7]);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Butterfly sum over `width` lanes (a power of two <= 64) that differ only in
+// the low log2(width) bits of the lane id.  Every lane ends with the same
+// bits: at each stage the two partners add the same two values.
+template <int WIDTH>
+__device__ __forceinline__ float xor_sum(float v) {
+#pragma unroll
+  for (int off = WIDTH / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float xor_max(float v) {
+#pragma unroll
+  for (int off = WIDTH / 2; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace bi

@@ -1,0 +1,74 @@
+// Internal launchers of the library (host side).  Arguments are assumed to
+// have passed the checks of api.cpp; each launcher only enqueues kernels on
+// the given stream and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bi {
+
+// GEMM tile shape: one shape for every M (no split-K).
+constexpr int kGemmBM = 256;
+constexpr int kGemmBN = 256;
+constexpr int kGemmBK = 64;
+
+// Decode attention: fixed key/value split size.
+constexpr int kKvSplit = 256;
+
+// Prefill attention: key block size (blocks are aligned to absolute position 0).
+constexpr int kPrefillKeyBlock = 64;
+
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* y, int64_t rows,
+                          int64_t hidden, float eps, hipStream_t s);
+
+hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, uint16_t* C, int64_t M, int64_t N,
+                       int64_t K, hipStream_t s);
+hipError_t launch_gemm_w4(const uint16_t* A, const uint8_t* Wq, const uint16_t* Ws, uint16_t* C,
+                          int64_t M, int64_t N, int64_t K, hipStream_t s);
+
+hipError_t launch_add(const uint16_t* x, const uint16_t* o, uint16_t* h, int64_t n, hipStream_t s);
+hipError_t launch_swiglu(const uint16_t* gu, uint16_t* act, int64_t rows, int64_t F, hipStream_t s);
+
+hipError_t launch_rope_kv(const uint16_t* qkv, const int32_t* pos, const int64_t* kv_row,
+                          uint16_t* q_out, uint16_t* k_pool, uint16_t* v_pool, int64_t rows,
+                          int Hq, int Hkv, int D, double theta, hipStream_t s);
+
+// Multi-sequence prefill attention.  Sequence descriptors live in device
+// memory (PrefillSeq array d_seqs), or, for one sequence, are passed by value
+// (d_seqs == nullptr, h_single != nullptr).  The host passes the largest
+// number of query tiles any sequence needs, for the grid only.
+struct PrefillSeq {
+  int64_t q_row;     // first row of the sequence's queries in q / o
+  int64_t kv_base;   // cache row of the sequence's position 0
+  int32_t q_start;   // absolute position of its first query
+  int32_t q_len;     // number of queries (>= 1)
+};
+int prefill_positions_per_tile(int group);
+hipError_t launch_attn_prefill(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_cache,
+                               const uint16_t* v_cache, uint16_t* o, int64_t o_row_stride,
+                               const PrefillSeq* d_seqs, const PrefillSeq* h_single, int n_seqs,
+                               int max_tiles, int Hq, int Hkv, int D, float scale, hipStream_t s);
+
+// Decode attention.  Per request: query row, cache offset and length in
+// device memory.
+struct DecodeSeq {
+  int64_t q_row;      // row of the request's query in q / o
+  int64_t kv_offset;  // cache row of the request's key 0
+  int32_t kv_len;     // number of keys (>= 1)
+  int32_t pad;
+};
+size_t decode_workspace_bytes(int B, int64_t max_kv_len, int Hq, int D);
+hipError_t launch_attn_decode(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_all,
+                              const uint16_t* v_all, const DecodeSeq* d_seqs, int B,
+                              int64_t max_kv_len, int Hq, int Hkv, int D, float scale, void* ws,
+                              uint16_t* o, int64_t o_row_stride, hipStream_t s);
+// Variant for the standalone entry point: separate offset / length arrays.
+hipError_t launch_attn_decode_arrays(const uint16_t* q, const uint16_t* k_all,
+                                     const uint16_t* v_all, const int64_t* kv_offset,
+                                     const int32_t* kv_len, int B, int64_t max_kv_len, int Hq,
+                                     int Hkv, int D, float scale, void* ws, uint16_t* o,
+                                     hipStream_t s);
+
+}  // namespace bi

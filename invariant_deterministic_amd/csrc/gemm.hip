@@ -1,0 +1,234 @@
+// Batch-invariant GEMM C = A * W^T for gfx950 (bf16 weights, and int4 weights
+// de-quantised inside the kernel).
+//
+// Matrix multiplication is one of the operations the M-0002 record
+// ("Deterministic and bit-exact inference", field `technical`) makes
+// batch-invariant.  The invariance argument here:
+//  * one tile shape (256 x 256 x 64) and one instruction stream for every M:
+//    there is no M-dependent dispatch, no split-K and no stream-K, and rows
+//    past M are handled by clamping their loads and masking their stores in
+//    the same instruction stream;
+//  * each C[i, j] is accumulated by one lane of one MFMA chain: K is walked in
+//    64-wide steps in ascending order, each step as four 16-deep
+//    v_mfma_f32_32x32x16_bf16 instructions in ascending order;
+//  * the MFMA unit treats every (row, column) slot of its 32 x 32 block the
+//    same way, so the bits of C[i, :] do not depend on which tile row or
+//    which slot row i lands in.
+// The tests check the last point empirically (every row at every position).
+//
+// Int4 weights ("Residual nondeterminism" in the M-0002 limitations warns of
+// de-quantisation kernels with atomic additions): each thread expands one
+// 32-element group -- code * fp16 scale, exact in fp32, one rounding to bf16
+// -- straight into the same LDS tile the bf16 path uses, so the int4 GEMM is
+// bit-identical to the bf16 GEMM on the de-quantised weight.
+//
+// Data flow: global -> registers (prefetch of step k+1 during step k) -> LDS
+// (two stages, 16-byte chunks xor-swizzled by row to keep ds_read_b128
+// conflict-free) -> MFMA operands.  MFMA operand A is the weight tile, operand
+// B the activation tile, so each lane ends with 4 consecutive output columns
+// of one output row and stores them as one 8-byte write.
+#include "bi_dev.h"
+#include "bi_internal.h"
+
+namespace bi {
+namespace {
+
+constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
+constexpr int NT = 512;                 // 8 waves: 2 along N (128 each) x 4 along M (64 each)
+constexpr int TILE = BM * BK;           // bf16 elements of one operand tile (BM == BN)
+static_assert(BM == BN, "square tile assumed by the LDS layout");
+
+// Element offset of 16-byte chunk `chunk` (0..7) of tile row `row`.
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * BK + ((chunk ^ (row & 7)) << 3);
+}
+
+// Expand one int4 group (16 bytes = 32 codes, one fp16 scale) into four
+// bf16 16-byte chunks of tile row `row`: w = bf16(code * scale).
+__device__ __forceinline__ void dequant_group_to_lds(const uint4& rq, uint16_t rs, uint16_t* sW,
+                                                     int row, int half) {
+  const float s = float(__builtin_bit_cast(_Float16, rs));
+  const uint32_t words[4] = {rq.x, rq.y, rq.z, rq.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      // nibble e of the little-endian word is element 8c + e of the group
+      const int code = int(words[c] << (28 - 4 * e)) >> 28;
+      f[e] = float(code) * s;  // exact: |code| <= 8, s has 11 significant bits
+    }
+    *reinterpret_cast<uint4*>(sW + lds_off(row, half * 4 + c)) = pack8(f);
+  }
+}
+
+template <bool W4>
+__global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict__ A,
+                                                     const void* __restrict__ Wv,
+                                                     const uint16_t* __restrict__ Ws,
+                                                     uint16_t* __restrict__ C, int M, int N, int K,
+                                                     int tiles_n, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];
+
+  // Work-group -> tile.  Work-groups are dealt round-robin to the 8 XCDs;
+  // give each XCD a contiguous run of row-major tiles so tiles sharing A rows
+  // share an L2.  This only moves whole tiles between work-groups.
+  const int wg = blockIdx.x;
+  const int tile = (n_tiles % 8 == 0) ? (wg % 8) * (n_tiles / 8) + wg / 8 : wg;
+  const int tm = tile / tiles_n;
+  const int tn = tile % tiles_n;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wn = wave & 1;   // 128 output columns
+  const int wm = wave >> 1;  // 64 output rows
+
+  // ---- global load assignment
+  // A tile: 256 rows x 8 chunks; thread t loads chunk (t & 7) of rows (t >> 3) + 64 i.
+  // Rows past M (past N for W) are clamped: computed, never stored.
+  const int ld_chunk = t & 7;
+  const int ld_row = t >> 3;
+  const int a_last = M - 1, w_last = N - 1;
+  const uint16_t* a_base = A + ld_chunk * 8;
+  int a_r0 = min(tm * BM + ld_row, a_last), a_r1 = min(tm * BM + ld_row + 64, a_last);
+  int a_r2 = min(tm * BM + ld_row + 128, a_last), a_r3 = min(tm * BM + ld_row + 192, a_last);
+  const uint16_t* w_base = static_cast<const uint16_t*>(Wv) + ld_chunk * 8;
+  int w_r0 = min(tn * BN + ld_row, w_last), w_r1 = min(tn * BN + ld_row + 64, w_last);
+  int w_r2 = min(tn * BN + ld_row + 128, w_last), w_r3 = min(tn * BN + ld_row + 192, w_last);
+  const int q_row = t >> 1;  // int4: 256 rows x 2 groups of 32
+  const int q_half = t & 1;
+  const int q_r = min(tn * BN + q_row, w_last);
+  const uint8_t* q_src = static_cast<const uint8_t*>(Wv) + int64_t(q_r) * (K / 2) + q_half * 16;
+  const uint16_t* s_src = Ws + int64_t(q_r) * (K / 32) + q_half;
+
+  uint4 ra0, ra1, ra2, ra3, rw0, rw1, rw2, rw3, rq;
+  uint16_t rs = 0;
+
+#define BI_LOAD_GLOBAL(kt)                                                                  \
+  do {                                                                                      \
+    const int ko = (kt) * BK;                                                               \
+    ra0 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r0) * K + ko);                 \
+    ra1 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r1) * K + ko);                 \
+    ra2 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r2) * K + ko);                 \
+    ra3 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r3) * K + ko);                 \
+    if constexpr (!W4) {                                                                    \
+      rw0 = *reinterpret_cast<const uint4*>(w_base + int64_t(w_r0) * K + ko);               \
+      rw1 = *reinterpret_cast<const uint4*>(w_base + int64_t(w_r1) * K + ko);               \
+      rw2 = *reinterpret_cast<const uint4*>(w_base + int64_t(w_r2) * K + ko);               \
+      rw3 = *reinterpret_cast<const uint4*>(w_base + int64_t(w_r3) * K + ko);               \
+    } else {                                                                                \
+      rq = *reinterpret_cast<const uint4*>(q_src + (kt) * (BK / 2));                        \
+      rs = s_src[(kt) * (BK / 32)];                                                         \
+    }                                                                                       \
+  } while (0)
+
+#define BI_STORE_LDS(stage)                                                                 \
+  do {                                                                                      \
+    uint16_t* sA = smem[stage][0];                                                          \
+    uint16_t* sW = smem[stage][1];                                                          \
+    *reinterpret_cast<uint4*>(sA + lds_off(ld_row, ld_chunk)) = ra0;                        \
+    *reinterpret_cast<uint4*>(sA + lds_off(ld_row + 64, ld_chunk)) = ra1;                   \
+    *reinterpret_cast<uint4*>(sA + lds_off(ld_row + 128, ld_chunk)) = ra2;                  \
+    *reinterpret_cast<uint4*>(sA + lds_off(ld_row + 192, ld_chunk)) = ra3;                  \
+    if constexpr (!W4) {                                                                    \
+      *reinterpret_cast<uint4*>(sW + lds_off(ld_row, ld_chunk)) = rw0;                      \
+      *reinterpret_cast<uint4*>(sW + lds_off(ld_row + 64, ld_chunk)) = rw1;                 \
+      *reinterpret_cast<uint4*>(sW + lds_off(ld_row + 128, ld_chunk)) = rw2;                \
+      *reinterpret_cast<uint4*>(sW + lds_off(ld_row + 192, ld_chunk)) = rw3;                \
+    } else {                                                                                \
+      dequant_group_to_lds(rq, rs, sW, q_row, q_half);                                      \
+    }                                                                                       \
+  } while (0)
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[bn][bm][r] = 0.f;
+
+  const int KT = K / BK;
+  BI_LOAD_GLOBAL(0);
+  BI_STORE_LDS(0);
+  __syncthreads();
+
+  const int frag_row = lane & 31;
+  const int frag_chunk = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) BI_LOAD_GLOBAL(kt + 1);
+    const uint16_t* sA = smem[cur][0];
+    const uint16_t* sW = smem[cur][1];
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 wf[4], af[2];
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn)
+        wf[bn] = *reinterpret_cast<const bf16x8*>(
+            sW + lds_off(wn * 128 + bn * 32 + frag_row, kk * 2 + frag_chunk));
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+        af[bm] = *reinterpret_cast<const bf16x8*>(
+            sA + lds_off(wm * 64 + bm * 32 + frag_row, kk * 2 + frag_chunk));
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm)
+          acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[bn], af[bm], acc[bn][bm], 0, 0, 0);
+    }
+    if (kt + 1 < KT) BI_STORE_LDS(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: acc[bn][bm][r] is C[m][n] with
+  //   m = tile row base + wm*64 + bm*32 + (lane & 31)
+  //   n = tile col base + wn*128 + bn*32 + 8*(r/4) + 4*(lane/32) + (r%4)
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm) {
+    const int m = tm * BM + wm * 64 + bm * 32 + (lane & 31);
+    if (m >= M) continue;
+    uint16_t* crow = C + int64_t(m) * N;
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = tn * BN + wn * 128 + bn * 32 + 8 * q + 4 * (lane >> 5);
+        if (n < N) {
+          uint2 v;
+          v.x = pack2bf(acc[bn][bm][4 * q + 0], acc[bn][bm][4 * q + 1]);
+          v.y = pack2bf(acc[bn][bm][4 * q + 2], acc[bn][bm][4 * q + 3]);
+          *reinterpret_cast<uint2*>(crow + n) = v;
+        }
+      }
+    }
+  }
+#undef BI_LOAD_GLOBAL
+#undef BI_STORE_LDS
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, uint16_t* C, int64_t M, int64_t N,
+                       int64_t K, hipStream_t s) {
+  const int tiles_m = int((M + BM - 1) / BM);
+  const int tiles_n = int((N + BN - 1) / BN);
+  const int n_tiles = tiles_m * tiles_n;
+  hipLaunchKernelGGL(gemm_kernel<false>, dim3(n_tiles), dim3(NT), 0, s, A,
+                     static_cast<const void*>(W), static_cast<const uint16_t*>(nullptr), C, int(M),
+                     int(N), int(K), tiles_n, n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_w4(const uint16_t* A, const uint8_t* Wq, const uint16_t* Ws, uint16_t* C,
+                          int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  const int tiles_m = int((M + BM - 1) / BM);
+  const int tiles_n = int((N + BN - 1) / BN);
+  const int n_tiles = tiles_m * tiles_n;
+  hipLaunchKernelGGL(gemm_kernel<true>, dim3(n_tiles), dim3(NT), 0, s, A,
+                     static_cast<const void*>(Wq), Ws, C, int(M), int(N), int(K), tiles_n, n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace bi

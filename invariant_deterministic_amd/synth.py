@@ -22,6 +22,7 @@ __all__ = [
     "ones_bf16",
     "quantize_int4_g32",
     "uniform_ints",
+    "normal_bf16_device",
 ]
 
 
@@ -80,3 +81,16 @@ def uniform_ints(seed: int, count: int, lo: int, hi: int) -> np.ndarray:
     """``count`` integers drawn uniformly from [lo, hi] inclusive (int64)."""
     rng = np.random.default_rng(seed)
     return rng.integers(lo, hi + 1, size=count).astype(np.int64)
+
+
+def normal_bf16_device(seed: int, shape, sigma: float = 1.0, device="cuda"):
+    """Large seeded N(0, sigma) bf16 tensors drawn on the device (torch's Philox
+    generator), for inputs too big to draw on the host (KV caches).  The same
+    seed gives the same tensor on every run; tests copy the parts the checker
+    needs back to the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        x.mul_(sigma)
+    return x.to(torch.bfloat16)

@@ -1,0 +1,177 @@
+"""CPU tests of the C-ABI boundary: the library loads, exports every function
+include/bi.h declares, and its argument checks return the documented status
+without launching anything (no GPU is touched: every call here fails its
+checks before any HIP call, or is a host-only helper)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from invariant_deterministic_amd import bi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+P16 = ctypes.c_void_p(0x100000)     # aligned fake addresses: never dereferenced
+P16b = ctypes.c_void_p(0x200000)
+P16c = ctypes.c_void_p(0x300000)
+MIS = ctypes.c_void_p(0x100002)     # misaligned
+NUL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "bi.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = bi.lib()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(bi.exported_symbols()) == names
+
+
+def test_constants_and_build_id():
+    assert bi.kv_split_size() == 256
+    assert bi.gemm_tile() == (256, 256, 64)
+    bid = bi.build_id()
+    assert re.fullmatch(r"[0-9a-f]{16}", bid)
+    for code in range(7):
+        assert bi.status_str(code).startswith("BI_")
+
+
+def test_rmsnorm_checks():
+    L = bi.lib()
+    assert L.bi_rmsnorm(NUL, P16, P16b, 4, 256, 1e-6, NUL) == NULL
+    assert L.bi_rmsnorm(P16, P16b, P16c, 0, 256, 1e-6, NUL) == SHAPE
+    assert L.bi_rmsnorm(P16, P16b, P16c, 4, 12, 1e-6, NUL) == UNSUP
+    assert L.bi_rmsnorm(P16, P16b, P16c, 4, 16392, 1e-6, NUL) == UNSUP
+    assert L.bi_rmsnorm(P16, P16b, P16c, 4, 256, -1.0, NUL) == SHAPE
+    assert L.bi_rmsnorm(P16, P16b, P16c, 4, 256, float("nan"), NUL) == SHAPE
+    assert L.bi_rmsnorm(MIS, P16b, P16c, 4, 256, 1e-6, NUL) == ALIGN
+    assert L.bi_rmsnorm(P16, P16b, P16, 4, 256, 1e-6, NUL) == SHAPE  # in place not allowed
+
+
+def test_gemm_checks():
+    L = bi.lib()
+    assert L.bi_gemm(NUL, P16, P16b, 1, 8, 64, NUL) == NULL
+    assert L.bi_gemm(P16, P16b, P16c, 0, 8, 64, NUL) == SHAPE
+    assert L.bi_gemm(P16, P16b, P16c, 1, 12, 64, NUL) == UNSUP     # N % 8
+    assert L.bi_gemm(P16, P16b, P16c, 1, 8, 96, NUL) == UNSUP      # K % 64
+    assert L.bi_gemm(MIS, P16b, P16c, 1, 8, 64, NUL) == ALIGN
+    assert L.bi_gemm_w4(P16, P16b, NUL, P16c, 1, 8, 64, NUL) == NULL
+    assert L.bi_gemm_w4(P16, P16b, ctypes.c_void_p(0x400001), P16c, 1, 8, 64, NUL) == ALIGN
+    assert L.bi_gemm_w4(P16, P16b, P16c, P16, 1, 8, 32, NUL) == UNSUP
+
+
+def test_attention_checks():
+    L = bi.lib()
+    sc = 0.088
+    assert L.bi_attn_prefill(NUL, P16, P16b, P16c, 0, 10, 32, 8, 128, sc, NUL) == NULL
+    assert L.bi_attn_prefill(P16, P16, P16b, P16c, 0, 0, 32, 8, 128, sc, NUL) == SHAPE
+    assert L.bi_attn_prefill(P16, P16, P16b, P16c, -1, 4, 32, 8, 128, sc, NUL) == SHAPE
+    assert L.bi_attn_prefill(P16, P16, P16b, P16c, 0, 4, 32, 8, 96, sc, NUL) == UNSUP
+    assert L.bi_attn_prefill(P16, P16, P16b, P16c, 0, 4, 32, 4, 128, sc, NUL) == UNSUP  # group 8
+    assert L.bi_attn_prefill(P16, P16, P16b, P16c, 0, 4, 30, 8, 128, sc, NUL) == SHAPE
+    assert L.bi_attn_prefill(P16, P16, P16b, P16c, 0, 4, 32, 8, 128, 0.0, NUL) == SHAPE
+    assert L.bi_attn_prefill(MIS, P16, P16b, P16c, 0, 4, 32, 8, 128, sc, NUL) == ALIGN
+    need = L.bi_attn_decode_workspace(4, 1000, 32, 128)
+    assert need >= 4 * 32 * 4 * 130 * 4
+    args = lambda ws, nbytes, B=4, maxl=1000, D=128: (P16, P16b, P16c, P16, P16b, B, maxl, 32, 8, D, sc, ws,
+                                                     nbytes, P16c, NUL)
+    assert L.bi_attn_decode(*args(NUL, need)) == WS
+    assert L.bi_attn_decode(*args(P16, need - 1)) == WS
+    assert L.bi_attn_decode(*args(P16, need, B=0)) == SHAPE
+    assert L.bi_attn_decode(*args(P16, need, maxl=0)) == SHAPE
+    assert L.bi_attn_decode(*args(P16, need, D=80)) == UNSUP
+    assert L.bi_attn_decode(NUL, P16b, P16c, P16, P16b, 4, 1000, 32, 8, 128, sc, P16, need, P16c, NUL) == NULL
+
+
+def test_elementwise_checks():
+    L = bi.lib()
+    assert L.bi_add(P16, P16b, P16c, 12, NUL) == UNSUP
+    assert L.bi_add(P16, NUL, P16c, 16, NUL) == NULL
+    assert L.bi_swiglu(P16, P16b, 4, 12, NUL) == UNSUP
+    assert L.bi_rope_kv(P16, P16b, P16c, P16, P16b, P16c, 4, 32, 8, 96, 1e6, NUL) == UNSUP
+    assert L.bi_rope_kv(P16, P16b, P16c, P16, P16b, P16c, 4, 32, 8, 128, -1.0, NUL) == SHAPE
+
+
+SEQS = [dict(q_len=1, ctx_len=700, kv_base=0), dict(q_len=250, ctx_len=250, kv_base=1000),
+        dict(q_len=1, ctx_len=0, kv_base=5000)]
+
+
+def test_step_pack_layout():
+    n_tok = sum(s["q_len"] for s in SEQS)
+    nbytes = bi.lib().bi_step_meta_bytes(len(SEQS), n_tok)
+    buf = np.zeros(nbytes, np.uint8)
+    arr = bi._seq_array(SEQS)
+    assert bi.lib().bi_step_pack(arr, len(SEQS), ctypes.c_void_p(buf.ctypes.data), nbytes - 1) == WS
+    assert bi.lib().bi_step_pack(arr, len(SEQS), ctypes.c_void_p(buf.ctypes.data), nbytes) == OK
+    hdr = buf[:32].view(np.int64)
+    assert list(hdr) == [3, n_tok, 1, 2]
+    # prefill list at 256: {q_row, kv_base, q_start, q_len}
+    pf = buf[256:256 + 24]
+    assert pf[:16].view(np.int64).tolist() == [1, 1000] and pf[16:24].view(np.int32).tolist() == [250, 250]
+    dec_off = 256 + 256
+    d0 = buf[dec_off:dec_off + 24]
+    assert d0[:16].view(np.int64).tolist() == [0, 0] and d0[16:20].view(np.int32)[0] == 701
+    d1 = buf[dec_off + 24:dec_off + 48]
+    assert d1[:16].view(np.int64).tolist() == [251, 5000] and d1[16:20].view(np.int32)[0] == 1
+    pos_off = dec_off + 256
+    pos = buf[pos_off:pos_off + 4 * n_tok].view(np.int32)
+    assert pos[0] == 700 and pos[1] == 250 and pos[250] == 499 and pos[251] == 0
+    kv_off = pos_off + ((4 * n_tok + 255) // 256) * 256
+    kvr = buf[kv_off:kv_off + 8 * n_tok].view(np.int64)
+    assert kvr[0] == 700 and kvr[1] == 1250 and kvr[250] == 1499 and kvr[251] == 5000
+
+
+def test_step_pack_rejects_bad_steps():
+    L = bi.lib()
+    buf = np.zeros(1 << 16, np.uint8)
+    for bad in ([dict(q_len=0, ctx_len=0, kv_base=0)], [dict(q_len=1, ctx_len=-1, kv_base=0)],
+                [dict(q_len=1, ctx_len=0, kv_base=-5)]):
+        assert L.bi_step_pack(bi._seq_array(bad), 1, ctypes.c_void_p(buf.ctypes.data), buf.size) == SHAPE
+    assert L.bi_step_pack(bi._seq_array(SEQS), 0, ctypes.c_void_p(buf.ctypes.data), buf.size) == SHAPE
+    assert L.bi_step_meta_bytes(0, 10) == 0
+
+
+def test_block_workspace_layout():
+    cfg = bi.BlockConfig(2560, 32, 8, 128, 9728, 1e-6, 1e6)
+    lay = bi.block_workspace(cfg, SEQS)
+    M = 252
+    offs = [lay.n1, lay.qkv, lay.q, lay.attn, lay.o, lay.h, lay.n2, lay.gu, lay.act, lay.d, lay.decode_partials]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.qkv - lay.n1 >= M * 2560 * 2 and lay.act - lay.gu >= M * 2 * 9728 * 2
+    assert lay.total >= lay.decode_partials + bi.attn_decode_workspace(2, 701, 32, 128)
+    nf = bi.block_workspace(bi.BlockConfig(256, 4, 4, 64, 0), [dict(q_len=128, ctx_len=0, kv_base=0)])
+    assert nf.h == ctypes.c_size_t(-1).value and nf.decode_partials == ctypes.c_size_t(-1).value
+
+
+def test_block_forward_checks():
+    L = bi.lib()
+    cfg = bi.BlockConfig(2560, 32, 8, 128, 9728, 1e-6, 1e6).c()
+    w = bi.bi_block_weights()
+    w.gamma1 = P16; w.gamma2 = P16
+    for f in ("qkv", "o", "gate_up", "down"):
+        setattr(w, f, bi.bi_weight(0x500000, None))
+    arr = bi._seq_array(SEQS)
+    pool = bi.bi_kv_pool(0x600000, 0x700000, 6000)
+    lay = bi.block_workspace(bi.BlockConfig(2560, 32, 8, 128, 9728, 1e-6, 1e6), SEQS)
+    call = lambda cfg_=cfg, w_=w, pool_=pool, meta=P16, x=P16b, y=P16c, ws=P16, nbytes=lay.total: L.bi_block_forward(
+        ctypes.byref(cfg_), ctypes.byref(w_), arr, 3, meta, ctypes.byref(pool_), x, y, ws, nbytes, NUL)
+    assert call(nbytes=lay.total - 1) == WS
+    assert call(meta=NUL) == NULL
+    assert call(y=P16b) == SHAPE                       # y aliases x
+    assert call(pool_=bi.bi_kv_pool(0x600000, 0x700000, 5000)) == SHAPE  # last sequence needs row 5000
+    w2 = bi.bi_block_weights.from_buffer_copy(w); w2.down = bi.bi_weight(None, None)
+    assert call(w_=w2) == NULL
+    bad = bi.BlockConfig(2560, 32, 8, 96, 9728).c()
+    assert call(cfg_=bad) == UNSUP
+    bad = bi.BlockConfig(2560, 32, 8, 128, 9728 + 8).c()
+    assert call(cfg_=bad) == UNSUP
+    w4 = bi.BlockConfig(2560, 32, 8, 128, 9728, int4=True).c()
+    assert call(cfg_=w4) == NULL                        # int4 weights need scales

@@ -78,3 +78,35 @@ def assert_within_tolerance(gpu_bits, ref_bits, what: str = ""):
     rep = tolerance_report(gpu_bits, ref_bits)
     assert rep["violations"] == 0, f"{what}: {rep}"
     return rep
+
+
+def rowwise_norm_report(gpu_bits, ref_bits, rel: float = REL_TOL):
+    """End-to-end rule for a composed block: per output row r,
+    ||gpu[r] - ref[r]||_2 <= rel * ||ref[r]||_2, and no NaN/Inf.
+
+    A block chains bf16-rounded stages; where fp32 accumulation and the fp64
+    checker round an intermediate element to neighbouring bf16 values, the next
+    K-long contraction spreads that one-ulp difference over its outputs, so
+    near-zero elements of the block output can differ by a few ulps of their
+    row's scale.  The per-element rule is applied stage by stage (each kernel
+    fed identical inputs); end to end the same relative tolerance is applied
+    to each token's output vector as a whole.
+    """
+    g = bf16_value(gpu_bits).reshape(len(gpu_bits), -1)
+    r = bf16_value(ref_bits).reshape(len(ref_bits), -1)
+    if not (np.isfinite(g).all() and np.isfinite(r).all()):
+        return {"rows": len(g), "bad_rows": -1, "nonfinite": True}
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.linalg.norm(r, axis=1)
+    ratio = num / np.maximum(den, 1e-30)
+    elem = tolerance_report(gpu_bits, ref_bits, rel)
+    return {"rows": len(g), "bad_rows": int((ratio > rel).sum()), "max_row_rel": float(ratio.max()),
+            "mean_row_rel": float(ratio.mean()), "elementwise_violations": elem["violations"],
+            "elements": elem["n"], "bitwise_equal": elem["bitwise_equal"]}
+
+
+def assert_rowwise_norm(gpu_bits, ref_bits, what: str = ""):
+    rep = rowwise_norm_report(gpu_bits, ref_bits)
+    print(f"{what} end-to-end: {rep}")
+    assert rep["bad_rows"] == 0, f"{what}: {rep}"
+    return rep
