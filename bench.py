@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Bench of the batch-invariant forward path on one MI355X.
+
+Default (the one JSON line the driver reads): the int4-weight decoder block
+(hidden 4096, 32/8 heads of 128, RoPE 1e6, SwiGLU 12288, symmetric int4 group
+32 with fp16 scales) on a mixed step of 256 decode requests with cached
+lengths drawn uniformly from 512..8192 plus one 2048-token prefill chunk.
+A step is one bi_block_forward call: RMSNorm, int4 GEMMs, RoPE + KV append,
+prefill attention, split-256 decode attention + combine, residual, SwiGLU.
+Inputs are seeded and synthetic and already resident in HBM when timing
+starts.  The decode attention streams ~4.6 GB of KV per step, far more than
+the 256 MB Infinity Cache, so weights are not served from it across steps.
+
+`--config` selects other workloads for profiling (they print their own line):
+dense (hidden 2560 block, 4000 tokens), gemm (K = N = 4096), decode (B = 64,
+L ~ U{1..32768}), norm (65536 x 4096), tiny (hidden 256 block, B = 8).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # B/s, MI355X HBM3E
+PEAK_BF16 = 2.5e15         # flop/s, dense bf16 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="mixed", choices=["mixed", "dense", "gemm", "decode", "norm", "tiny"])
+    p.add_argument("--batch", type=int, default=256, help="decode requests in the mixed step")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--kernel-reps", type=int, default=10)
+    return p.parse_args()
+
+
+# --------------------------------------------------------------- helpers
+def event_time_ms(torch, fn, reps):
+    """Average duration of fn() (kernels on torch's current stream) with HIP events."""
+    s = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    start.record(s)
+    for _ in range(reps):
+        fn()
+    end.record(s)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def time_steps(torch, step, steps, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3
+
+
+def cpu_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        return cpu_cores()
+
+
+# ------------------------------------------------------------ workloads
+def mixed_workload(torch, bi, synth, B):
+    H, F, hq, hkv, d = 4096, 12288, 32, 8, 128
+    w = dict(gamma1=synth.ones_bf16(H), gamma2=synth.ones_bf16(H),
+             w_qkv=synth.quantize_int4_g32(504, (hq + 2 * hkv) * d, H),
+             w_o=synth.quantize_int4_g32(505, H, hq * d),
+             w_gate_up=synth.quantize_int4_g32(506, 2 * F, H),
+             w_down=synth.quantize_int4_g32(508, H, F))
+    wd = {k: bi.to_dev(v) if not isinstance(v, tuple) else
+          (torch.from_numpy(v[0]).cuda(), torch.from_numpy(v[1].view("int16")).cuda()) for k, v in w.items()}
+    cfg = bi.BlockConfig(H, hq, hkv, d, F, 1e-6, 1e6, int4=True)
+    blk = bi.Block(cfg, wd)
+    lens = synth.uniform_ints(501, B, 512, 8192)
+    cap = 8192 + 1
+    rows = B * cap + 2048
+    kp = synth.normal_bf16_device(509, (rows, hkv, d))
+    vp = synth.normal_bf16_device(510, (rows, hkv, d))
+    seqs = [dict(q_len=1, ctx_len=int(lens[b]), kv_base=b * cap) for b in range(B)]
+    seqs.append(dict(q_len=2048, ctx_len=0, kv_base=B * cap))
+    x = bi.to_dev(__import__("numpy").concatenate([synth.normal_bf16(502, (B, H)),
+                                                   synth.normal_bf16(503, (2048, H))]))
+    return dict(cfg=cfg, w_host=w, w_dev=wd, blk=blk, lens=lens, cap=cap, kp=kp, vp=vp, seqs=seqs, x=x,
+                H=H, F=F, hq=hq, hkv=hkv, d=d, B=B)
+
+
+def block_flops_bytes(H, F, hq, hkv, d, tokens, weight_bytes, prefill_T, decode_lens):
+    """Algorithmic work of one block step (roofline model)."""
+    lin = 2.0 * tokens * (H * (hq + 2 * hkv) * d + hq * d * H + H * 2 * F + F * H)
+    pairs = prefill_T * (prefill_T + 1) / 2.0
+    att_pf = 4.0 * d * hq * pairs
+    dec_bytes = sum(2.0 * (L + 1) * hkv * d * 2 for L in decode_lens)
+    io_bytes = 2.0 * tokens * H * 2 + tokens * 2 * hkv * d * 2
+    t_roof = (max(lin / PEAK_BF16, weight_bytes / PEAK_HBM) + att_pf / PEAK_BF16
+              + dec_bytes / PEAK_HBM + io_bytes / PEAK_HBM)
+    return lin, att_pf, dec_bytes, t_roof
+
+
+def run_mixed(args, torch, bi, synth):
+    import numpy as np
+    W = mixed_workload(torch, bi, synth, args.batch)
+    blk, x, seqs, kp, vp = W["blk"], W["x"], W["seqs"], W["kp"], W["vp"]
+    meta, _ = bi.step_meta(seqs, x.device)
+    lay = bi.block_workspace(W["cfg"], seqs)
+    ws = torch.empty(lay.total, dtype=torch.uint8, device=x.device)
+    y = torch.empty_like(x)
+
+    def step():
+        blk.forward(x, seqs, kp, vp, y=y, ws=ws, meta=meta)
+
+    ms = time_steps(torch, step, args.steps, args.warmup)
+    tokens = args.batch + 2048
+    H, F, hq, hkv, d = W["H"], W["F"], W["hq"], W["hkv"], W["d"]
+    wbytes = sum(v[0].nbytes + v[1].nbytes for k, v in W["w_host"].items() if isinstance(v, tuple))
+    lin, att_pf, dec_bytes, t_roof = block_flops_bytes(H, F, hq, hkv, d, tokens, wbytes, 2048, W["lens"])
+
+    # ---- dominant kernels, timed alone on the step's own data and launch shape
+    M = tokens
+    n2 = bi.stage(ws, lay, "n2", M, H)
+    wgu = W["w_dev"]["w_gate_up"]
+    gu_out = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=x.device)
+    t_gu = event_time_ms(torch, lambda: bi.gemm_w4(n2, wgu[0], wgu[1], out=gu_out), args.kernel_reps)
+    gu_flops = 2.0 * M * 2 * F * H
+    q = bi.stage(ws, lay, "q", M, hq * d)[:args.batch]
+    offs = torch.tensor([s["kv_base"] for s in seqs[:-1]], dtype=torch.int64, device=x.device)
+    lens = torch.tensor([s["ctx_len"] + 1 for s in seqs[:-1]], dtype=torch.int32, device=x.device)
+    max_len = int(max(s["ctx_len"] + 1 for s in seqs[:-1]))
+    dws = torch.empty(bi.attn_decode_workspace(args.batch, max_len, hq, d), dtype=torch.uint8, device=x.device)
+    dout = torch.empty_like(q)
+    t_dec = event_time_ms(torch, lambda: bi.attn_decode(q, kp, vp, offs, lens, max_len, hq, hkv, d,
+                                                        1 / math.sqrt(d), ws=dws, out=dout), args.kernel_reps)
+    if t_dec >= t_gu:
+        roof = {"kernel": "decode attention (split-256 + combine)", "bound": "hbm",
+                "achieved": dec_bytes / (t_dec * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
+    else:
+        roof = {"kernel": "int4 GEMM gate/up (M=%d, N=%d, K=%d)" % (M, 2 * F, H), "bound": "mfma",
+                "achieved": gu_flops / (t_gu * 1e-3) / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel_ms"] = t_dec if roof["bound"] == "hbm" else t_gu
+
+    out = {
+        "metric": "batch-invariant block tokens/s",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 activations, int4 weights, fp32 accumulation", "data": "synthetic (seeded)",
+        "config": {"workload": "int4 block hidden 4096, FFN 12288, 32/8 heads x 128: mixed step of "
+                               f"{args.batch} decodes (KV 512..8192) + one 2048-token prefill chunk",
+                   "tokens_per_step": tokens, "decode_batch": args.batch, "prefill_chunk": 2048},
+        "roofline": roof,
+        "block_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms,
+                           "linear_gflop": lin / 1e9, "prefill_attn_gflop": att_pf / 1e9,
+                           "decode_kv_gb": dec_bytes / 1e9, "weight_mb": wbytes / 1e6},
+        "kernels_ms": {"gemm_w4_gate_up": t_gu, "attn_decode": t_dec},
+        "build_id": bi.build_id(),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_mixed(W, bi, torch)
+    return out
+
+
+def cpu_baseline_mixed(W, bi, torch):
+    """The oracle, as it stands, on a bounded sample of the same step: 8 decode
+    requests and a 128-token prefill chunk (same weights and KV distributions)."""
+    import numpy as np
+    import oracle
+    nd, T = 8, 128
+    seqs, kp_rows, xs = [], [], []
+    cap = W["cap"]
+    k_np, v_np = [], []
+    base = 0
+    x_host = bi.to_bits(W["x"])
+    for b in range(nd):
+        L = int(W["lens"][b])
+        kc = bi.to_bits(W["kp"][b * cap:b * cap + L])
+        vc = bi.to_bits(W["vp"][b * cap:b * cap + L])
+        k_np.append(np.concatenate([kc, np.zeros((1,) + kc.shape[1:], np.uint16)]))
+        v_np.append(np.concatenate([vc, np.zeros((1,) + vc.shape[1:], np.uint16)]))
+        seqs.append(dict(q_len=1, ctx_len=L, kv_base=base))
+        base += L + 1
+        xs.append(x_host[b:b + 1])
+    k_np.append(np.zeros((T, W["hkv"], W["d"]), np.uint16))
+    v_np.append(np.zeros((T, W["hkv"], W["d"]), np.uint16))
+    seqs.append(dict(q_len=T, ctx_len=0, kv_base=base))
+    xs.append(x_host[W["B"]:W["B"] + T])
+    kpool, vpool = np.concatenate(k_np), np.concatenate(v_np)
+    cfg = dict(hidden=W["H"], n_q_heads=W["hq"], n_kv_heads=W["hkv"], head_dim=W["d"], ffn=W["F"],
+               eps=1e-6, rope_theta=1e6)
+    x = np.concatenate(xs)
+    t0 = time.perf_counter()
+    oracle.block_forward(cfg, W["w_host"], x, seqs, kpool, vpool)
+    dt = time.perf_counter() - t0
+    return {"value": (nd + T) / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{nd} decode requests (KV {min(W['lens'][:nd])}..{max(W['lens'][:nd])}) + one "
+                      f"{T}-token prefill chunk of the same block, fp64 numpy, {dt:.1f} s",
+            "host_cores": cpu_cores()}
+
+
+# --------------------------------------------- auxiliary workloads (profiling)
+def run_gemm(args, torch, bi, synth):
+    K = N = 4096
+    A = synth.normal_bf16_device(201, (4096, K))
+    Ws = [synth.normal_bf16_device(202 + i, (N, K)) for i in range(12)]  # rotate: 12 x 32 MB > MALL
+    res = {}
+    for M in (1, 7, 64, 513, 4096):
+        a = A[:M].contiguous()
+        c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        it = iter(range(10 ** 9))
+        t = event_time_ms(torch, lambda: bi.gemm(a, Ws[next(it) % 12], out=c), max(args.kernel_reps, 24))
+        fl = 2.0 * M * N * K
+        by = 2.0 * (M * K + N * K + M * N)
+        res[M] = {"ms": t, "tflops": fl / t / 1e9, "gbs": by / t / 1e6,
+                  "frac": max(fl / PEAK_BF16, by / PEAK_HBM) / (t * 1e-3)}
+    return {"metric": "bf16 GEMM K=N=4096 (no split-K, one tile)", "value": res[4096]["tflops"],
+            "unit": "TFLOP/s", "config": {"workload": "C = A W^T, K = N = 4096, M in 1,7,64,513,4096"},
+            "per_m": res, "build_id": bi.build_id()}
+
+
+def run_decode(args, torch, bi, synth):
+    import numpy as np
+    hq, hkv, d, B = 32, 8, 128, 64
+    lens = synth.uniform_ints(401, B, 1, 32768)
+    total = int(lens.sum())
+    k = synth.normal_bf16_device(403, (total, hkv, d))
+    v = synth.normal_bf16_device(404, (total, hkv, d))
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    q = bi.to_dev(synth.normal_bf16(402, (B, hq * d)))
+    od = torch.from_numpy(offs).cuda()
+    ld = torch.from_numpy(lens.astype(np.int32)).cuda()
+    ws = torch.empty(bi.attn_decode_workspace(B, 32768, hq, d), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    t = event_time_ms(torch, lambda: bi.attn_decode(q, k, v, od, ld, 32768, hq, hkv, d, 1 / math.sqrt(d),
+                                                    ws=ws, out=out), max(args.kernel_reps, 20))
+    by = float(lens.sum()) * hkv * d * 2 * 2
+    return {"metric": "decode attention GB/s (split 256)", "value": by / t / 1e6, "unit": "GB/s",
+            "ms": t, "frac": by / t / 1e6 / (PEAK_HBM / 1e9),
+            "config": {"workload": "B=64, L~U{1..32768}, 32/8 heads x 128"}, "build_id": bi.build_id()}
+
+
+def run_norm(args, torch, bi, synth):
+    M, H = 65536, 4096
+    x = synth.normal_bf16_device(1200, (M, H))
+    g = bi.to_dev(synth.normal_bf16(1201, (H,), 0.02, 1.0))
+    y = torch.empty_like(x)
+    t = event_time_ms(torch, lambda: bi.rmsnorm(x, g, 1e-6, out=y), max(args.kernel_reps, 20))
+    by = 2.0 * M * H * 2
+    return {"metric": "RMSNorm GB/s", "value": by / t / 1e6, "unit": "GB/s", "ms": t,
+            "frac": by / t / 1e6 / (PEAK_HBM / 1e9), "config": {"workload": "65536 x 4096"},
+            "build_id": bi.build_id()}
+
+
+def run_dense(args, torch, bi, synth):
+    import numpy as np
+    H, F, hq, hkv, d = 2560, 9728, 32, 8, 128
+    w = dict(gamma1=synth.ones_bf16(H), gamma2=synth.ones_bf16(H),
+             w_qkv=synth.normal_bf16(302, ((hq + 2 * hkv) * d, H), 0.02),
+             w_o=synth.normal_bf16(303, (H, hq * d), 0.02),
+             w_gate_up=synth.normal_bf16(304, (2 * F, H), 0.02),
+             w_down=synth.normal_bf16(306, (H, F), 0.02))
+    blk = bi.Block(bi.BlockConfig(H, hq, hkv, d, F, 1e-6, 1e6), {k: bi.to_dev(v) for k, v in w.items()})
+    x = bi.to_dev(synth.normal_bf16(301, (4000, H)))
+    kp = torch.zeros((4000, hkv, d), dtype=torch.bfloat16, device="cuda")
+    vp = torch.zeros_like(kp)
+    res = {}
+    for chunk in (4000, 1000, 250):
+        plans = []
+        for s0 in range(0, 4000, chunk):
+            seqs = [dict(q_len=chunk, ctx_len=s0, kv_base=0)]
+            meta, _ = bi.step_meta(seqs)
+            lay = bi.block_workspace(blk.cfg, seqs)
+            plans.append((x[s0:s0 + chunk], seqs, meta, torch.empty(lay.total, dtype=torch.uint8, device="cuda")))
+
+        def prefill():
+            for xs, seqs, meta, ws in plans:
+                blk.forward(xs, seqs, kp, vp, ws=ws, meta=meta)
+        ms = time_steps(torch, prefill, args.steps, args.warmup)
+        wbytes = sum(v.nbytes for k, v in w.items() if k.startswith("w_"))
+        lin, att, _, t_roof = block_flops_bytes(H, F, hq, hkv, d, 4000, wbytes * (4000 // chunk), 4000, [])
+        res[chunk] = {"ms": ms, "tokens_per_s": 4000 / (ms * 1e-3), "roofline_frac": t_roof * 1e3 / ms}
+    return {"metric": "batch-invariant block tokens/s (dense hidden 2560, 4000-token prefill)",
+            "value": res[4000]["tokens_per_s"], "unit": "tokens/s", "per_chunk": res,
+            "config": {"workload": "dense bf16 block hidden 2560, FFN 9728, 32/8 x 128, 4000 tokens"},
+            "build_id": bi.build_id()}
+
+
+def run_tiny(args, torch, bi, synth):
+    import numpy as np
+    H = 256
+    w = dict(gamma1=synth.ones_bf16(H), w_qkv=synth.normal_bf16(102, (768, H), 0.02),
+             w_o=synth.normal_bf16(103, (H, 256), 0.02))
+    blk = bi.Block(bi.BlockConfig(H, 4, 4, 64, 0), {k: bi.to_dev(v) for k, v in w.items()})
+    res = {}
+    for B in (1, 3, 8):
+        x = bi.to_dev(synth.normal_bf16(101, (128 * B, H)))
+        kp = torch.zeros((128 * B, 4, 64), dtype=torch.bfloat16, device="cuda")
+        vp = torch.zeros_like(kp)
+        seqs = [dict(q_len=128, ctx_len=0, kv_base=128 * i) for i in range(B)]
+        meta, _ = bi.step_meta(seqs)
+        lay = bi.block_workspace(blk.cfg, seqs)
+        ws = torch.empty(lay.total, dtype=torch.uint8, device="cuda")
+        ms = time_steps(torch, lambda: blk.forward(x, seqs, kp, vp, ws=ws, meta=meta), args.steps, args.warmup)
+        res[B] = {"ms": ms, "tokens_per_s": 128 * B / (ms * 1e-3)}
+    return {"metric": "tiny block tokens/s", "value": res[8]["tokens_per_s"], "unit": "tokens/s",
+            "per_batch": res, "config": {"workload": "hidden 256, 4 heads x 64, T=128 per sequence"},
+            "build_id": bi.build_id()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from invariant_deterministic_amd import bi, synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    bi.lib()
+    fn = {"mixed": run_mixed, "dense": run_dense, "gemm": run_gemm, "decode": run_decode,
+          "norm": run_norm, "tiny": run_tiny}[args.config]
+    out = fn(args, torch, bi, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

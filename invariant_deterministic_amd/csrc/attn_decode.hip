@@ -9,21 +9,20 @@
 // are merged in ascending s by a second kernel, so a request's bits never
 // depend on the batch, the other requests' lengths or the grid.
 //
-// Split kernel: one 256-thread work-group per (unit s, kv head g, request b).
-// Each wave streams 64 of the unit's keys; lane l takes the 16-byte chunk
-// l % (D/8) of key l / (D/8) of each wave-wide load, so one load instruction
-// covers D/8 * 16 bytes of each of 64/(D/8) keys.  For the G query heads that
-// share kv head g:
-//   score = (q_scaled . k) by an fmaf chain over the lane's 8 dims, then an xor
-//           butterfly over the D/8 lanes of the key (fixed tree);
-//   m     = exact maximum over the unit (order-free);
-//   p     = exp2(score - m); l = sum of p; o = sum of p * v, each summed per
-//           lane in ascending key order, then by xor butterflies across the
-//           key groups of the wave, then across the 4 waves in ascending
-//           order through LDS.
-// Partials (m, l, o[D]) go to the workspace in fp32.  Scores are in log2
-// units (q is pre-multiplied by scale * log2(e)), so exp2 is the native
-// instruction.  Keys past L_b are neither loaded nor counted (p = 0).
+// Split kernel: one 256-thread work-group per (kv head g, unit s, request b);
+// each wave owns 64 of the unit's keys.  For the G query heads sharing kv
+// head g:
+//   scores  S^T = K Q^T on v_mfma_f32_16x16x32_bf16, the keys streamed from
+//           HBM straight into the MFMA operand layout (16 keys x 32 dims per
+//           operand, D/32 steps in ascending order), times scale * log2(e);
+//   m       exact maximum over the unit (order-free);
+//   p       exp2(score - m), staged in LDS; l = sum of p (fixed in-lane order,
+//           xor lanes 16 and 32, then waves 0..3);
+//   o       sum of p * v on the VALU: lane (key group kl, dims 8 dc..) walks
+//           its keys in ascending order with fmaf; the per-(wave, key group)
+//           partials are then added in one fixed order through LDS.
+// Partials (m, l, o[D]) go to the workspace in fp32.  Keys past L_b are
+// neither loaded nor counted (score -inf, p = 0, value 0).
 //
 // Combine kernel: one thread per (request, head, dim) walks s = 0 .. S_b - 1
 // in ascending order: M = max m_s; w_s = exp2(m_s - M); O = sum w_s o_s,
@@ -44,15 +43,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t* __restrict__ v_all, const DecodeSeq* __restrict__ seqs, int Hkv,
     int64_t max_len, int max_splits, float qscale, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
-  constexpr int CH = D / 8;      // lanes per key row
-  constexpr int KPL = 64 / CH;   // keys per wave-wide load
+  constexpr int KS = D / 32;     // MFMA k-steps over the head dimension
+  constexpr int CH = D / 8;      // lanes per key row in the value pass
+  constexpr int KPL = 64 / CH;   // keys per wave-wide value load
   constexpr int NIT = kKeysPerWave / KPL;
+  static_assert(G <= 16, "one 16-wide MFMA column block holds the group's heads");
   __shared__ float s_m[kWavesPerUnit][G];
   __shared__ float s_l[kWavesPerUnit][G];
-  __shared__ float s_o[kWavesPerUnit][G][D];
+  __shared__ __attribute__((aligned(16))) float s_p[kWavesPerUnit][kKeysPerWave][G];
+  __shared__ float s_o[kWavesPerUnit][KPL][G][D];
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y;
+  const int g = blockIdx.x;   // kv heads of one key block are dispatched together
+  const int s = blockIdx.y;
   const int b = blockIdx.z;
   const DecodeSeq sq = seqs[b];
   const int64_t L = sq.kv_len;
@@ -62,89 +64,84 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
+  const int l16 = lane & 15;
+  const int grp = lane >> 4;
+  const int Hq = Hkv * G;
+  const int64_t row_stride = int64_t(Hkv) * D;
+  const int64_t key_base = int64_t(s) * kSplit + w * kKeysPerWave;
+
+  // ---- S^T = K Q^T with v_mfma_f32_16x16x32_bf16, straight from HBM.
+  // A operand (keys): lane holds K[key_base + 16 kb + l16][32 ks + 8 grp .. + 8]
+  // B operand (heads): lane holds Q[head l16][32 ks + 8 grp .. + 8] (0 past G)
+  const uint16_t* kb_ptr = k_all + (sq.kv_offset + key_base + l16) * row_stride + g * D + grp * 8;
+  uint4 kr[4][KS];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const bool valid = key_base + 16 * kb + l16 < L;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kr[kb][ks] = valid ? ld_stream16(kb_ptr + int64_t(16 * kb) * row_stride + 32 * ks)
+                         : make_uint4(0, 0, 0, 0);
+  }
+  bf16x8 qb[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (l16 < G) v = *reinterpret_cast<const uint4*>(q + sq.q_row * q_stride + (g * G + l16) * D + 32 * ks + grp * 8);
+    qb[ks] = as_bf16x8(v);
+  }
+  f32x4 sacc[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[kb][ks]), qb[ks], sacc[kb], 0, 0, 0);
+  }
+
+  // value loads go out now; their latency overlaps the softmax
   const int dc = lane % CH;
   const int kl = lane / CH;
-  const int Hq = Hkv * G;
-
-  // queries of the G heads of group g, dims dc*8 .. dc*8+7, times scale*log2(e)
-  float qf[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(q + sq.q_row * q_stride + (g * G + h) * D + dc * 8);
-    unpack8(raw, qf[h]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[h][e] *= qscale;
-  }
-
-  const int64_t row_stride = int64_t(Hkv) * D;
-  const uint16_t* kb = k_all + sq.kv_offset * row_stride + g * D + dc * 8;
-  const uint16_t* vb = v_all + sq.kv_offset * row_stride + g * D + dc * 8;
-  const int64_t key0 = int64_t(s) * kSplit + w * kKeysPerWave + kl;
-
-  // ---- scores
-  uint4 kr[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int64_t key = key0 + it * KPL;
-    kr[it] = key < L ? ld_stream16(kb + key * row_stride)
-                     : make_uint4(0, 0, 0, 0);
-  }
-  float sc[NIT][G];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    float kf[8];
-    unpack8(kr[it], kf);
-    const bool valid = key0 + it * KPL < L;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float d = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) d = __builtin_fmaf(qf[h][e], kf[e], d);
-#pragma unroll
-      for (int off = CH / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off, 64);
-      sc[it][h] = valid ? d : -INFINITY;
-    }
-  }
-
-  // ---- exact maximum of the unit
-  float m[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mx = sc[0][h];
-#pragma unroll
-    for (int it = 1; it < NIT; ++it) mx = fmaxf(mx, sc[it][h]);
-#pragma unroll
-    for (int off = CH; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    if (lane == 0) s_m[w][h] = mx;
-  }
-
-  // issue the value loads before waiting on the other waves
+  const uint16_t* vb_ptr = v_all + (sq.kv_offset + key_base + kl) * row_stride + g * D + dc * 8;
   uint4 vr[NIT];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int64_t key = key0 + it * KPL;
-    vr[it] = key < L ? ld_stream16(vb + key * row_stride)
-                     : make_uint4(0, 0, 0, 0);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    m[h] = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
-
-  // ---- weights and their sum (ascending key order within the lane)
-  float lsum[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) lsum[h] = 0.f;
-#pragma unroll
   for (int it = 0; it < NIT; ++it)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p = __builtin_amdgcn_exp2f(sc[it][h] - m[h]);
-      sc[it][h] = p;
-      lsum[h] += p;
-    }
+    vr[it] = key_base + it * KPL + kl < L ? ld_stream16(vb_ptr + int64_t(it * KPL) * row_stride)
+                                          : make_uint4(0, 0, 0, 0);
 
-  // ---- weighted values
+  // ---- scores: lane holds head l16, keys key_base + 16 kb + 4 grp + r
+  float sc[4][4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool valid = key_base + 16 * kb + 4 * grp + r < L;
+      const float v = valid ? sacc[kb][r] * qscale : -INFINITY;
+      sc[kb][r] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  if (grp == 0 && l16 < G) s_m[w][l16] = mx;
+  __syncthreads();
+  const int hh = l16 < G ? l16 : 0;
+  const float m = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
+  float ls = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(sc[kb][r] - m);
+      ls += p;
+      if (l16 < G) s_p[w][16 * kb + 4 * grp + r][l16] = p;
+    }
+  ls += __shfl_xor(ls, 16, 64);
+  ls += __shfl_xor(ls, 32, 64);
+  if (grp == 0 && l16 < G) s_l[w][l16] = ls;
+  __syncthreads();
+
+  // ---- weighted values: lane takes dims 8 dc .. + 8 of keys kl, kl + KPL, ...
   float oacc[G][8];
 #pragma unroll
   for (int h = 0; h < G; ++h)
@@ -154,41 +151,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   for (int it = 0; it < NIT; ++it) {
     float vf[8];
     unpack8(vr[it], vf);
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) oacc[h][e] = __builtin_fmaf(sc[it][h], vf[e], oacc[h][e]);
-  }
-
-  // ---- across the key groups of the wave (lanes with equal dc), fixed tree
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int off = CH; off < 64; off <<= 1) lsum[h] += __shfl_xor(lsum[h], off, 64);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int off = CH; off < 64; off <<= 1) oacc[h][e] += __shfl_xor(oacc[h][e], off, 64);
-  }
-  if (kl == 0) {
+    const float* pp = s_p[w][it * KPL + kl];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
+      const float p = pp[h];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[w][h][dc * 8 + e] = oacc[h][e];
-      if (dc == 0) s_l[w][h] = lsum[h];
+      for (int e = 0; e < 8; ++e) oacc[h][e] = __builtin_fmaf(p, vf[e], oacc[h][e]);
     }
   }
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_o[w][kl][h][dc * 8 + e] = oacc[h][e];
   __syncthreads();
 
-  // ---- across the 4 waves in ascending order; write the unit's partials
+  // ---- fixed-order sum over (wave, key group); write the unit's partials
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int h = i / D;
     const int d = i % D;
-    const float o = ((s_o[0][h][d] + s_o[1][h][d]) + s_o[2][h][d]) + s_o[3][h][d];
+    float o = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWavesPerUnit; ++ww)
+#pragma unroll
+      for (int k = 0; k < KPL; ++k) o += s_o[ww][k][h][d];
     const int64_t slot = (int64_t(b) * Hq + g * G + h) * max_splits + s;
     ws_o[slot * D + d] = o;
     if (d == 0) {
-      ws_ml[slot * 2 + 0] = m[h];
+      ws_ml[slot * 2 + 0] = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
       ws_ml[slot * 2 + 1] = ((s_l[0][h] + s_l[1][h]) + s_l[2][h]) + s_l[3][h];
     }
   }
@@ -242,7 +231,7 @@ hipError_t launch_split(const uint16_t* q, int64_t q_stride, const uint16_t* k_a
                         const uint16_t* v_all, const DecodeSeq* seqs, int B, int64_t max_len,
                         int max_splits, int Hkv, float qscale, float* ws_o, float* ws_ml,
                         hipStream_t s) {
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(max_splits, Hkv, B), dim3(256), 0, s, q,
+  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(Hkv, max_splits, B), dim3(256), 0, s, q,
                      q_stride, k_all, v_all, seqs, Hkv, max_len, max_splits, qscale, ws_o, ws_ml);
   return hipGetLastError();
 }

@@ -9,10 +9,10 @@
 // absolute position t computes is a function of t and of the keys 0..t.
 //  * Keys are processed in blocks of 64 aligned to absolute position 0,
 //    block j = keys [64 j, 64 j + 64), in ascending j, with an online softmax.
-//  * Queries are processed in wave tiles of 64 positions, also aligned to
-//    absolute position 0.  A wave tile whose first position is 64 i visits
-//    key blocks 0..i, so query t visits blocks 0..floor(t / 64) whatever the
-//    chunk it arrived in; keys after t inside block floor(t/64) are masked.
+//  * Queries are processed in wave tiles of 32 positions, also aligned to
+//    absolute position 0.  A wave tile at position 32 i visits key blocks
+//    0..floor(32 i / 64), so query t visits blocks 0..floor(t / 64) whatever
+//    the chunk it arrived in; keys after t inside that block are masked.
 //  * Rows of a tile outside the chunk (before its first position or after its
 //    last) are computed with zero queries and never stored; keys at or after
 //    the end of the chunk are not read (zero in LDS) and are always masked.
@@ -27,9 +27,10 @@
 // Scores are in log2 units (scale * log2(e) applied to S in fp32).  The final
 // output is bf16(O / l).
 //
-// Work-group = 4 waves = (kv head g, tile of P = 256 / G positions): wave w
-// takes query head g*G + w % G and positions tile + 64 (w / G).  The waves
-// share the K / V^T blocks in LDS (double-buffered through registers).
+// Work-group = 8 waves = (kv head g, tile of P = 256 / G positions): wave w
+// takes query head g*G + w % G and the 32 positions tile + 32 (w / G).  The
+// waves share the K / V^T blocks in LDS (double-buffered through registers;
+// waves 0-3 move K, waves 4-7 move V and transpose it four keys at a time).
 #include "bi_dev.h"
 #include "bi_internal.h"
 
@@ -37,8 +38,9 @@ namespace bi {
 namespace {
 
 constexpr int KB = kPrefillKeyBlock;  // 64 keys per block
-constexpr int QW = 64;                // query positions per wave
-constexpr int NTH = 256;
+constexpr int QW = 32;                // query positions per wave
+constexpr int NW = 8;                 // waves per work-group
+constexpr int NTH = NW * 64;
 
 // K block in LDS: [64 keys][D], 16-byte chunks xor-swizzled by key.
 template <int D>
@@ -55,11 +57,12 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, uint16_t* __restrict__ o, int64_t o_stride,
     const PrefillSeq* __restrict__ seqs, PrefillSeq single, int Hkv, float sscale) {
-  constexpr int P = QW * 4 / G;       // positions per work-group tile
+  constexpr int P = QW * NW / G;      // positions per work-group tile
   constexpr int DCH = D / 8;          // 16-byte chunks per row
   constexpr int KK = D / 16;          // MFMA k-steps for S
   constexpr int BD = D / 32;          // output blocks along D
-  constexpr int LD_IT = KB * DCH / NTH;  // chunks per thread per block (K and V each)
+  constexpr int KPT = KB * DCH / 256; // K chunks (waves 0-3) / V keys (waves 4-7) per thread
+  static_assert(KPT == 2 || KPT == 4, "value transpose handles 2 or 4 keys per thread");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][KB * D];
 
@@ -77,7 +80,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
   const int lane = t & 63;
   const int w = t >> 6;
   const int h = g * G + (w % G);
-  const int wpos = tile_pos + QW * (w / G);       // first position of this wave's tile
+  const int wpos = tile_pos + QW * (w / G);        // first position of this wave's queries
   const bool wave_active = wpos <= last_pos && wpos + QW - 1 >= sq.q_start;
   const int wave_last_blk = wpos / KB;             // diagonal block of the wave
   const int n_blk = min(tile_pos + P - 1, last_pos) / KB + 1;  // blocks the work-group loads
@@ -85,69 +88,77 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
 
   const int l32 = lane & 31;
   const int hf = lane >> 5;
-  const int Hq = Hkv * G;
   const int64_t kv_stride = int64_t(Hkv) * D;
 
   // ---- queries of this wave: B operand of S^T = K Q^T, lane holds
-  // Q[pos = wpos + 32 bq + l32][dims (2 kk + hf) * 8 .. + 8]
-  bf16x8 qf[2][KK];
-#pragma unroll
-  for (int bq = 0; bq < 2; ++bq) {
-    const int pos = wpos + 32 * bq + l32;
+  // Q[pos = wpos + l32][dims (2 kk + hf) * 8 .. + 8]
+  bf16x8 qf[KK];
+  {
+    const int pos = wpos + l32;
     const bool in = pos >= sq.q_start && pos <= last_pos;
     const uint16_t* src = q + (sq.q_row + (pos - sq.q_start)) * q_stride + h * D + hf * 8;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       uint4 v = make_uint4(0, 0, 0, 0);
       if (in) v = *reinterpret_cast<const uint4*>(src + kk * 16);
-      qf[bq][kk] = as_bf16x8(v);
+      qf[kk] = as_bf16x8(v);
     }
   }
 
-  // ---- key/value block loads: thread t moves chunks c = t + 256 i of the block
-  const uint16_t* kbase = k_cache + sq.kv_base * kv_stride + int64_t(g) * D;
-  const uint16_t* vbase = v_cache + sq.kv_base * kv_stride + int64_t(g) * D;
-  uint4 rk[LD_IT], rv[LD_IT];
+  // ---- block loads.  Waves 0-3 move K: thread u = t (0..255) takes chunk u %
+  // DCH of keys u / DCH + (256 / DCH) i.  Waves 4-7 move V: thread u = t - 256
+  // takes chunk u % DCH of the KPT consecutive keys KPT (u / DCH) .., which it
+  // transposes in registers into KPT-key rows of V^T.
+  const bool is_k = w < 4;
+  const int u = t & 255;
+  const int uc = u % DCH;
+  const int ur = u / DCH;
+  const uint16_t* kbase = k_cache + sq.kv_base * kv_stride + int64_t(g) * D + uc * 8;
+  const uint16_t* vbase = v_cache + sq.kv_base * kv_stride + int64_t(g) * D + uc * 8;
+  uint4 rr[KPT];
   auto load_block = [&](int blk) {
 #pragma unroll
-    for (int i = 0; i < LD_IT; ++i) {
-      const int c = t + NTH * i;
-      const int key = blk * KB + c / DCH;
-      const int ch = c % DCH;
-      if (key < kv_valid) {
-        rk[i] = *reinterpret_cast<const uint4*>(kbase + int64_t(key) * kv_stride + ch * 8);
-        rv[i] = *reinterpret_cast<const uint4*>(vbase + int64_t(key) * kv_stride + ch * 8);
-      } else {
-        rk[i] = make_uint4(0, 0, 0, 0);
-        rv[i] = make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < KPT; ++i) {
+      const int key = blk * KB + (is_k ? ur + (256 / DCH) * i : KPT * ur + i);
+      rr[i] = make_uint4(0, 0, 0, 0);
+      if (key < kv_valid)
+        rr[i] = *reinterpret_cast<const uint4*>((is_k ? kbase : vbase) + int64_t(key) * kv_stride);
     }
   };
   auto store_block = [&](int stage) {
+    if (is_k) {
 #pragma unroll
-    for (int i = 0; i < LD_IT; ++i) {
-      const int c = t + NTH * i;
-      const int key = c / DCH;
-      const int ch = c % DCH;
-      *reinterpret_cast<uint4*>(&sK[stage][k_off<D>(key, ch)]) = rk[i];
-      const uint32_t wv[4] = {rv[i].x, rv[i].y, rv[i].z, rv[i].w};
+      for (int i = 0; i < KPT; ++i)
+        *reinterpret_cast<uint4*>(&sK[stage][k_off<D>(ur + (256 / DCH) * i, uc)]) = rr[i];
+    } else {
+      // rr[i] holds dims 8 uc .. + 8 of key KPT ur + i; row d of V^T gets the
+      // KPT keys' values of dim d (2 bytes each, ascending key).
+      const uint32_t* w32 = reinterpret_cast<const uint32_t*>(rr);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sV[stage][vt_off(ch * 8 + 2 * e, key)] = uint16_t(wv[e] & 0xFFFF);
-        sV[stage][vt_off(ch * 8 + 2 * e + 1, key)] = uint16_t(wv[e] >> 16);
+      for (int e = 0; e < 8; ++e) {
+        const int d = uc * 8 + e;
+        // 16-bit element e of key i sits in word 4 i + e / 2, half e % 2
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        if constexpr (KPT == 4) {
+          uint2 v;
+          v.x = __builtin_amdgcn_perm(w32[4 + e / 2], w32[0 + e / 2], sel);
+          v.y = __builtin_amdgcn_perm(w32[12 + e / 2], w32[8 + e / 2], sel);
+          *reinterpret_cast<uint2*>(&sV[stage][vt_off(d, KPT * ur)]) = v;
+        } else {
+          const uint32_t v = __builtin_amdgcn_perm(w32[4 + e / 2], w32[0 + e / 2], sel);
+          *reinterpret_cast<uint32_t*>(&sV[stage][vt_off(d, KPT * ur)]) = v;
+        }
       }
     }
   };
 
-  f32x16 acc_o[BD][2];
+  f32x16 acc_o[BD];
 #pragma unroll
   for (int bd = 0; bd < BD; ++bd)
 #pragma unroll
-    for (int bq = 0; bq < 2; ++bq)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[bd][bq][r] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) acc_o[bd][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
 
   load_block(0);
   store_block(0);
@@ -159,62 +170,53 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     if (wave_active && blk <= wave_last_blk) {
       const uint16_t* cK = sK[cur];
       const uint16_t* cV = sV[cur];
-      // S^T blocks: [bk: keys 32 bk ..][bq: queries 32 bq ..]
-      f32x16 s[2][2];
+      // S^T blocks [bk]: keys 32 bk .. of the block, queries of the wave
+      f32x16 s[2];
 #pragma unroll
       for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-        for (int bq = 0; bq < 2; ++bq)
+        for (int r = 0; r < 16; ++r) s[bk][r] = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[bk][bq][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
+      for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
         for (int bk = 0; bk < 2; ++bk) {
-          const bf16x8 kf =
-              *reinterpret_cast<const bf16x8*>(cK + k_off<D>(32 * bk + l32, 2 * kk + hf));
-#pragma unroll
-          for (int bq = 0; bq < 2; ++bq)
-            s[bk][bq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[bq][kk], s[bk][bq], 0, 0, 0);
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cK + k_off<D>(32 * bk + l32, 2 * kk + hf));
+          s[bk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[bk], 0, 0, 0);
         }
-      }
-      // scale, mask, online softmax.  Lane holds query wpos + 32 bq + l32 and
-      // keys blk*64 + 32 bk + 8 (r / 4) + 4 hf + r % 4.
+      // scale, mask, online softmax.  Lane holds query wpos + l32 and keys
+      // blk*64 + 32 bk + 8 (r / 4) + 4 hf + r % 4.
       const bool diag = blk == wave_last_blk;
+      const int qpos = wpos + l32;
+      float mx = -INFINITY;
 #pragma unroll
-      for (int bq = 0; bq < 2; ++bq) {
-        const int qpos = wpos + 32 * bq + l32;
-        float mx = -INFINITY;
+      for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-        for (int bk = 0; bk < 2; ++bk)
+        for (int r = 0; r < 16; ++r) {
+          const int key = blk * KB + 32 * bk + 8 * (r >> 2) + 4 * hf + (r & 3);
+          float v = s[bk][r] * sscale;
+          if (diag && (key > qpos || key >= kv_valid)) v = -INFINITY;
+          s[bk][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float rs = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = blk * KB + 32 * bk + 8 * (r >> 2) + 4 * hf + (r & 3);
-            float v = s[bk][bq][r] * sscale;
-            if (diag && (key > qpos || key >= kv_valid)) v = -INFINITY;
-            s[bk][bq][r] = v;
-            mx = fmaxf(mx, v);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run[bq], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[bq] - m_new);
-        m_run[bq] = m_new;
-        float rs = 0.f;
+      for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-        for (int bk = 0; bk < 2; ++bk)
+        for (int r = 0; r < 16; ++r) {
+          const float pv = __builtin_amdgcn_exp2f(s[bk][r] - m_new);
+          s[bk][r] = pv;
+          rs += pv;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l_run = l_run * alpha + rs;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pv = __builtin_amdgcn_exp2f(s[bk][bq][r] - m_new);
-            s[bk][bq][r] = pv;
-            rs += pv;
-          }
-        rs += __shfl_xor(rs, 32, 64);
-        l_run[bq] = l_run[bq] * alpha + rs;
+      for (int bd = 0; bd < BD; ++bd)
 #pragma unroll
-        for (int bd = 0; bd < BD; ++bd)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc_o[bd][bq][r] *= alpha;
-      }
+        for (int r = 0; r < 16; ++r) acc_o[bd][r] *= alpha;
       // O^T[d][q] += V^T[d][key] P^T[key][q].  P (fp32) enters the bf16 MFMA as
       // two bf16 terms, P = hi + lo with hi = bf16(P), lo = bf16(P - hi), so
       // the weights carry ~16 significant bits; each k-step adds V hi, then
@@ -226,32 +228,25 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int key_a = 32 * bk + 16 * half + 4 * hf;
-          bf16x8 p_hi[2], p_lo[2];
+          uint32_t hw[4], lw[4];
 #pragma unroll
-          for (int bq = 0; bq < 2; ++bq) {
-            uint32_t hw[4], lw[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float a = s[bk][bq][8 * half + 2 * e];
-              const float b = s[bk][bq][8 * half + 2 * e + 1];
-              const uint32_t hp = pack2bf(a, b);
-              hw[e] = hp;
-              lw[e] = pack2bf(a - bf2f_lo(hp), b - bf2f_hi(hp));
-            }
-            p_hi[bq] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-            p_lo[bq] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+          for (int e = 0; e < 4; ++e) {
+            const float a = s[bk][8 * half + 2 * e];
+            const float b = s[bk][8 * half + 2 * e + 1];
+            const uint32_t hp = pack2bf(a, b);
+            hw[e] = hp;
+            lw[e] = pack2bf(a - bf2f_lo(hp), b - bf2f_hi(hp));
           }
+          const bf16x8 p_hi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+          const bf16x8 p_lo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
 #pragma unroll
           for (int bd = 0; bd < BD; ++bd) {
             const int d = 32 * bd + l32;
             const uint2 lo = *reinterpret_cast<const uint2*>(cV + vt_off(d, key_a));
             const uint2 hi = *reinterpret_cast<const uint2*>(cV + vt_off(d, key_a + 8));
             const bf16x8 vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-            for (int bq = 0; bq < 2; ++bq) {
-              acc_o[bd][bq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_hi[bq], acc_o[bd][bq], 0, 0, 0);
-              acc_o[bd][bq] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_lo[bq], acc_o[bd][bq], 0, 0, 0);
-            }
+            acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_hi, acc_o[bd], 0, 0, 0);
+            acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_lo, acc_o[bd], 0, 0, 0);
           }
         }
     }
@@ -260,25 +255,22 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
   }
 
   if (!wave_active) return;
-  // ---- normalise and store: lane holds query wpos + 32 bq + l32 and dims
+  // ---- normalise and store: lane holds query wpos + l32 and dims
   // 32 bd + 8 (r / 4) + 4 hf + r % 4 (4 consecutive dims per register group).
+  const int pos = wpos + l32;
+  if (pos < sq.q_start || pos > last_pos) return;
+  const float inv = 1.0f / l_run;
+  uint16_t* dst = o + (sq.q_row + (pos - sq.q_start)) * o_stride + h * D;
 #pragma unroll
-  for (int bq = 0; bq < 2; ++bq) {
-    const int pos = wpos + 32 * bq + l32;
-    if (pos < sq.q_start || pos > last_pos) continue;
-    const float inv = 1.0f / l_run[bq];
-    uint16_t* dst = o + (sq.q_row + (pos - sq.q_start)) * o_stride + h * D;
+  for (int bd = 0; bd < BD; ++bd)
 #pragma unroll
-    for (int bd = 0; bd < BD; ++bd)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d = 32 * bd + 8 * rg + 4 * hf;
-        uint2 v;
-        v.x = pack2bf(acc_o[bd][bq][4 * rg + 0] * inv, acc_o[bd][bq][4 * rg + 1] * inv);
-        v.y = pack2bf(acc_o[bd][bq][4 * rg + 2] * inv, acc_o[bd][bq][4 * rg + 3] * inv);
-        *reinterpret_cast<uint2*>(dst + d) = v;
-      }
-  }
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d = 32 * bd + 8 * rg + 4 * hf;
+      uint2 v;
+      v.x = pack2bf(acc_o[bd][4 * rg + 0] * inv, acc_o[bd][4 * rg + 1] * inv);
+      v.y = pack2bf(acc_o[bd][4 * rg + 2] * inv, acc_o[bd][4 * rg + 3] * inv);
+      *reinterpret_cast<uint2*>(dst + d) = v;
+    }
 }
 
 template <int D, int G>
@@ -292,7 +284,7 @@ hipError_t launch_t(const uint16_t* q, int64_t q_stride, const uint16_t* k, cons
 
 }  // namespace
 
-int prefill_positions_per_tile(int group) { return QW * 4 / group; }
+int prefill_positions_per_tile(int group) { return QW * NW / group; }
 
 hipError_t launch_attn_prefill(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_cache,
                                const uint16_t* v_cache, uint16_t* o, int64_t o_row_stride,
