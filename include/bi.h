@@ -222,7 +222,7 @@ typedef struct {
  * uploads those bytes to device memory (e.g. through pinned memory) and
  * passes the device address to bi_block_forward together with the same host
  * bi_seq array.  This keeps every call free of hidden synchronisation.      */
-size_t bi_step_meta_bytes(int n_seqs, int64_t n_tokens);
+size_t bi_step_meta_bytes(const bi_seq* seqs, int n_seqs); /* 0 if the step is invalid */
 bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t bytes);
 
 /* Offsets (bytes into the block workspace) of every intermediate stage, for

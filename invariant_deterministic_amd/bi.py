@@ -78,7 +78,7 @@ _SIGNATURES = {
     "bi_attn_decode_workspace": (c_size_t, [c_int, c_int64, c_int, c_int]),
     "bi_attn_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int,
                                c_int, c_int, c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
-    "bi_step_meta_bytes": (c_size_t, [c_int, c_int64]),
+    "bi_step_meta_bytes": (c_size_t, [ctypes.POINTER(bi_seq), c_int]),
     "bi_step_pack": (c_int, [ctypes.POINTER(bi_seq), c_int, c_void_p, c_size_t]),
     "bi_block_workspace": (c_int, [ctypes.POINTER(bi_block_cfg), ctypes.POINTER(bi_seq), c_int,
                                    ctypes.POINTER(bi_block_ws_layout)]),
@@ -270,8 +270,7 @@ def _seq_array(seqs):
 def step_meta(seqs, device="cuda"):
     """Pack a step description on the host and upload it (a device uint8 tensor)."""
     arr = _seq_array(seqs)
-    n_tok = sum(int(s["q_len"]) for s in seqs)
-    nbytes = lib().bi_step_meta_bytes(len(seqs), n_tok)
+    nbytes = lib().bi_step_meta_bytes(arr, len(seqs))
     if nbytes == 0:
         raise BiError("bi_step_meta_bytes: invalid step")
     host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=torch.cuda.is_available())

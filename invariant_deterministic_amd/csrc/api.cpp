@@ -10,6 +10,8 @@
 
 #include <algorithm>
 
+#include <hip/hip_vector_types.h>
+
 #include "../../include/bi.h"
 #include "bi_internal.h"
 
@@ -63,16 +65,26 @@ bool scale_ok(float s) { return s > 0.f && s < 3.0e38f; }
 
 // ---- step metadata layout (host bytes uploaded by the caller)
 struct MetaLayout {
-  size_t prefill, decode, pos, kv, total;
+  size_t prefill, decode, pos, kv, units, total;
 };
-MetaLayout meta_layout(int n_seqs, int64_t n_tokens) {
+// Layout of the packed step description: header, prefill descriptors, decode
+// descriptors, per-row positions, per-row KV rows, then the decode unit list
+// (one (request, unit) int32 pair per 256 keys of each decode request).
+MetaLayout meta_layout(int n_seqs, int64_t n_tokens, int64_t n_units) {
   MetaLayout L;
   L.prefill = 256;
   L.decode = L.prefill + align256(size_t(n_seqs) * sizeof(PrefillSeq));
   L.pos = L.decode + align256(size_t(n_seqs) * sizeof(DecodeSeq));
   L.kv = L.pos + align256(size_t(n_tokens) * sizeof(int32_t));
-  L.total = L.kv + align256(size_t(n_tokens) * sizeof(int64_t));
+  L.units = L.kv + align256(size_t(n_tokens) * sizeof(int64_t));
+  L.total = L.units + align256(size_t(n_units) * 8);
   return L;
+}
+int64_t decode_units(const bi_seq* seqs, int n_seqs) {
+  int64_t u = 0;
+  for (int i = 0; i < n_seqs; ++i)
+    if (seqs[i].q_len == 1) u += (int64_t(seqs[i].ctx_len) + 1 + bi::kKvSplit - 1) / bi::kKvSplit;
+  return u;
 }
 
 struct StepSummary {
@@ -310,9 +322,10 @@ bi_status bi_attn_decode(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* 
                                                 Hq, Hkv, D, scale, ws, o, stream));
 }
 
-size_t bi_step_meta_bytes(int n_seqs, int64_t n_tokens) {
-  if (n_seqs < 1 || n_tokens < 1) return 0;
-  return meta_layout(n_seqs, n_tokens).total;
+size_t bi_step_meta_bytes(const bi_seq* seqs, int n_seqs) {
+  StepSummary s;
+  if (summarize(seqs, n_seqs, &s) != BI_OK) return 0;
+  return meta_layout(n_seqs, s.M, decode_units(seqs, n_seqs)).total;
 }
 
 bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t bytes) {
@@ -320,7 +333,9 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
   bi_status st = summarize(seqs, n_seqs, &s);
   if (st != BI_OK) return st;
   if (!host_meta) return BI_ERR_NULL;
-  const MetaLayout L = meta_layout(n_seqs, s.M);
+  const int64_t n_units = decode_units(seqs, n_seqs);
+  if (n_units > INT32_MAX) return BI_ERR_UNSUPPORTED;
+  const MetaLayout L = meta_layout(n_seqs, s.M, n_units);
   if (bytes < L.total) return BI_ERR_WORKSPACE;
   memset(host_meta, 0, L.total);
   int64_t* hdr = at<int64_t>(host_meta, 0);
@@ -328,6 +343,9 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
   hdr[1] = s.M;
   hdr[2] = s.n_prefill;
   hdr[3] = s.n_decode;
+  hdr[4] = n_units;
+  int32_t* units = at<int32_t>(host_meta, L.units);
+  int64_t u = 0;
   PrefillSeq* pf = at<PrefillSeq>(host_meta, L.prefill);
   DecodeSeq* dc = at<DecodeSeq>(host_meta, L.decode);
   int32_t* pos = at<int32_t>(host_meta, L.pos);
@@ -342,6 +360,11 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
       d.kv_offset = q.kv_base;
       d.kv_len = q.ctx_len + 1;
       d.pad = 0;
+      const int64_t nu = (int64_t(d.kv_len) + bi::kKvSplit - 1) / bi::kKvSplit;
+      for (int64_t k = 0; k < nu; ++k, ++u) {
+        units[2 * u] = nd;
+        units[2 * u + 1] = int32_t(k);
+      }
       dc[nd++] = d;
     } else {
       PrefillSeq p;
@@ -406,7 +429,9 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
   const int64_t M = s.M;
   const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, F = c.ffn;
   const int qkv_n = (Hq + 2 * Hkv) * D;
-  const MetaLayout ML = meta_layout(n_seqs, M);
+  const int64_t n_units = decode_units(seqs, n_seqs);
+  if (n_units > INT32_MAX) return BI_ERR_UNSUPPORTED;
+  const MetaLayout ML = meta_layout(n_seqs, M, n_units);
   uint16_t* n1 = at<uint16_t>(ws, L.pub.n1);
   uint16_t* qkv = at<uint16_t>(ws, L.pub.qkv);
   uint16_t* q = at<uint16_t>(ws, L.pub.q);
@@ -440,7 +465,8 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
   }
   if (s.n_decode) {
     BI_TRY(bi::launch_attn_decode(q, int64_t(Hq) * D, kv->k, kv->v, at<DecodeSeq>(d_meta, ML.decode),
-                                  s.n_decode, s.max_decode_len, Hq, Hkv, D, scale,
+                                  at<int2>(d_meta, ML.units), int(n_units), s.n_decode,
+                                  s.max_decode_len, Hq, Hkv, D, scale,
                                   at<void>(ws, L.pub.decode_partials), attn, int64_t(Hq) * D,
                                   stream));
   }

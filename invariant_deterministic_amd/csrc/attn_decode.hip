@@ -9,7 +9,9 @@
 // are merged in ascending s by a second kernel, so a request's bits never
 // depend on the batch, the other requests' lengths or the grid.
 //
-// Split kernel: one 256-thread work-group per (kv head g, unit s, request b);
+// Split kernel: one 256-thread work-group per (kv head g, unit s, request b)
+// (the block entry point passes a host-built list of the step's real units,
+// the standalone one launches the max-units grid and idle groups exit);
 // each wave owns 64 of the unit's keys.  For the G query heads sharing kv
 // head g:
 //   scores  S^T = K Q^T on v_mfma_f32_16x16x32_bf16, the keys streamed from
@@ -19,8 +21,9 @@
 //   p       exp2(score - m), staged in LDS; l = sum of p (fixed in-lane order,
 //           xor lanes 16 and 32, then waves 0..3);
 //   o       sum of p * v on the VALU: lane (key group kl, dims 8 dc..) walks
-//           its keys in ascending order with fmaf; the per-(wave, key group)
-//           partials are then added in one fixed order through LDS.
+//           its keys in ascending order with fmaf; the key groups of a wave
+//           are added by a fixed xor tree, the 4 waves in ascending order
+//           through LDS.
 // Partials (m, l, o[D]) go to the workspace in fp32.  Keys past L_b are
 // neither loaded nor counted (score -inf, p = 0, value 0).
 //
@@ -40,9 +43,9 @@ constexpr int kKeysPerWave = kSplit / kWavesPerUnit;
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_all,
-    const uint16_t* __restrict__ v_all, const DecodeSeq* __restrict__ seqs, int Hkv,
-    int64_t max_len, int max_splits, float qscale, float* __restrict__ ws_o,
-    float* __restrict__ ws_ml) {
+    const uint16_t* __restrict__ v_all, const DecodeSeq* __restrict__ seqs,
+    const int2* __restrict__ units, int Hkv, int64_t max_len, int max_splits, float qscale,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
   constexpr int KS = D / 32;     // MFMA k-steps over the head dimension
   constexpr int CH = D / 8;      // lanes per key row in the value pass
   constexpr int KPL = 64 / CH;   // keys per wave-wide value load
@@ -51,11 +54,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   __shared__ float s_m[kWavesPerUnit][G];
   __shared__ float s_l[kWavesPerUnit][G];
   __shared__ __attribute__((aligned(16))) float s_p[kWavesPerUnit][kKeysPerWave][G];
-  __shared__ float s_o[kWavesPerUnit][KPL][G][D];
+  __shared__ float s_o[kWavesPerUnit][G][D];
 
   const int g = blockIdx.x;   // kv heads of one key block are dispatched together
-  const int s = blockIdx.y;
-  const int b = blockIdx.z;
+  // (request, unit) from a host-built list of real units, or the full grid
+  const int b = units ? units[blockIdx.y].x : int(blockIdx.z);
+  const int s = units ? units[blockIdx.y].y : int(blockIdx.y);
   const DecodeSeq sq = seqs[b];
   const int64_t L = sq.kv_len;
   if (L < 1 || L > max_len) return;  // the combine kernel reports the request as NaN
@@ -159,21 +163,30 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
       for (int e = 0; e < 8; ++e) oacc[h][e] = __builtin_fmaf(p, vf[e], oacc[h][e]);
     }
   }
+  // key groups of the wave (lanes with equal dc) by a fixed xor tree, then
+  // one partial per wave through LDS
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_o[w][kl][h][dc * 8 + e] = oacc[h][e];
+    for (int e = 0; e < 8; ++e) {
+      float v = oacc[h][e];
+#pragma unroll
+      for (int off = CH; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
+      oacc[h][e] = v;
+    }
+  if (kl == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[w][h][dc * 8 + e] = oacc[h][e];
+  }
   __syncthreads();
 
-  // ---- fixed-order sum over (wave, key group); write the unit's partials
+  // ---- fixed-order sum over the waves; write the unit's partials
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int h = i / D;
     const int d = i % D;
-    float o = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWavesPerUnit; ++ww)
-#pragma unroll
-      for (int k = 0; k < KPL; ++k) o += s_o[ww][k][h][d];
+    const float o = ((s_o[0][h][d] + s_o[1][h][d]) + s_o[2][h][d]) + s_o[3][h][d];
     const int64_t slot = (int64_t(b) * Hq + g * G + h) * max_splits + s;
     ws_o[slot * D + d] = o;
     if (d == 0) {
@@ -228,11 +241,12 @@ __global__ void decode_pack_kernel(const int64_t* __restrict__ kv_offset,
 
 template <int D, int G>
 hipError_t launch_split(const uint16_t* q, int64_t q_stride, const uint16_t* k_all,
-                        const uint16_t* v_all, const DecodeSeq* seqs, int B, int64_t max_len,
-                        int max_splits, int Hkv, float qscale, float* ws_o, float* ws_ml,
-                        hipStream_t s) {
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(Hkv, max_splits, B), dim3(256), 0, s, q,
-                     q_stride, k_all, v_all, seqs, Hkv, max_len, max_splits, qscale, ws_o, ws_ml);
+                        const uint16_t* v_all, const DecodeSeq* seqs, const int2* units,
+                        int n_units, int B, int64_t max_len, int max_splits, int Hkv, float qscale,
+                        float* ws_o, float* ws_ml, hipStream_t s) {
+  const dim3 grid = units ? dim3(Hkv, n_units, 1) : dim3(Hkv, max_splits, B);
+  hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(256), 0, s, q, q_stride, k_all,
+                     v_all, seqs, units, Hkv, max_len, max_splits, qscale, ws_o, ws_ml);
   return hipGetLastError();
 }
 
@@ -249,9 +263,10 @@ size_t decode_workspace_bytes(int B, int64_t max_kv_len, int Hq, int D) {
 }
 
 hipError_t launch_attn_decode(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_all,
-                              const uint16_t* v_all, const DecodeSeq* d_seqs, int B,
-                              int64_t max_kv_len, int Hq, int Hkv, int D, float scale, void* ws,
-                              uint16_t* o, int64_t o_row_stride, hipStream_t s) {
+                              const uint16_t* v_all, const DecodeSeq* d_seqs, const int2* d_units,
+                              int n_units, int B, int64_t max_kv_len, int Hq, int Hkv, int D,
+                              float scale, void* ws, uint16_t* o, int64_t o_row_stride,
+                              hipStream_t s) {
   const int max_splits = int((max_kv_len + kSplit - 1) / kSplit);
   const size_t slots = size_t(B) * Hq * max_splits;
   float* ws_o = static_cast<float*>(ws);
@@ -261,8 +276,8 @@ hipError_t launch_attn_decode(const uint16_t* q, int64_t q_row_stride, const uin
   hipError_t e = hipErrorInvalidValue;
 #define BI_DEC(DD, GG)                                                                          \
   if (D == DD && G == GG)                                                                     \
-    e = launch_split<DD, GG>(q, q_row_stride, k_all, v_all, d_seqs, B, max_kv_len, max_splits, \
-                             Hkv, qscale, ws_o, ws_ml, s);
+    e = launch_split<DD, GG>(q, q_row_stride, k_all, v_all, d_seqs, d_units, n_units, B, \
+                             max_kv_len, max_splits, Hkv, qscale, ws_o, ws_ml, s);
   BI_DEC(64, 1) BI_DEC(64, 2) BI_DEC(64, 4) BI_DEC(64, 8)
   BI_DEC(128, 1) BI_DEC(128, 2) BI_DEC(128, 4) BI_DEC(128, 8)
 #undef BI_DEC
@@ -289,8 +304,8 @@ hipError_t launch_attn_decode_arrays(const uint16_t* q, const uint16_t* k_all,
                      B, seqs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_attn_decode(q, int64_t(Hq) * D, k_all, v_all, seqs, B, max_kv_len, Hq, Hkv, D,
-                            scale, ws, o, int64_t(Hq) * D, s);
+  return launch_attn_decode(q, int64_t(Hq) * D, k_all, v_all, seqs, nullptr, 0, B, max_kv_len,
+                            Hq, Hkv, D, scale, ws, o, int64_t(Hq) * D, s);
 }
 
 }  // namespace bi

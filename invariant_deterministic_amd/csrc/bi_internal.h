@@ -60,10 +60,13 @@ struct DecodeSeq {
   int32_t pad;
 };
 size_t decode_workspace_bytes(int B, int64_t max_kv_len, int Hq, int D);
+// d_units: optional device list of (request, unit) pairs to compute (n_units
+// of them); nullptr launches every (request, unit < max units) pair.
 hipError_t launch_attn_decode(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_all,
-                              const uint16_t* v_all, const DecodeSeq* d_seqs, int B,
-                              int64_t max_kv_len, int Hq, int Hkv, int D, float scale, void* ws,
-                              uint16_t* o, int64_t o_row_stride, hipStream_t s);
+                              const uint16_t* v_all, const DecodeSeq* d_seqs, const int2* d_units,
+                              int n_units, int B, int64_t max_kv_len, int Hq, int Hkv, int D,
+                              float scale, void* ws, uint16_t* o, int64_t o_row_stride,
+                              hipStream_t s);
 // Variant for the standalone entry point: separate offset / length arrays.
 hipError_t launch_attn_decode_arrays(const uint16_t* q, const uint16_t* k_all,
                                      const uint16_t* v_all, const int64_t* kv_offset,

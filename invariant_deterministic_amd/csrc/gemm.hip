@@ -24,9 +24,13 @@
 //
 // Data flow: global -> registers (prefetch of step k+1 during step k) -> LDS
 // (two stages, 16-byte chunks xor-swizzled by row to keep ds_read_b128
-// conflict-free) -> MFMA operands.  MFMA operand A is the weight tile, operand
-// B the activation tile, so each lane ends with 4 consecutive output columns
-// of one output row and stores them as one 8-byte write.
+// conflict-free) -> MFMA operands.  Inside a step the fragments of k-substep
+// kk+1 are read while the MFMAs of kk run, one LDS read between consecutive
+// MFMAs (scheduling hints), and the MFMA phase runs at raised wave priority
+// so the SIMD's other wave issues its memory work in the gaps.  MFMA operand
+// A is the weight tile, operand B the activation tile, so each lane ends with
+// 4 consecutive output columns of one output row and stores them as one
+// 8-byte write.
 #include "bi_dev.h"
 #include "bi_internal.h"
 
@@ -161,23 +165,41 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
     if (kt + 1 < KT) BI_LOAD_GLOBAL(kt + 1);
     const uint16_t* sA = smem[cur][0];
     const uint16_t* sW = smem[cur][1];
+    bf16x8 wf[2][4], af[2][2];
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+      af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 64 + bm * 32 + frag_row, frag_chunk));
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn)
+      wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + lds_off(wn * 128 + bn * 32 + frag_row, frag_chunk));
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 wf[4], af[2];
+      const int cb = kk & 1, nb = cb ^ 1;
+      if (kk + 1 < BK / 16) {
+        // read in the order the next substep uses them: A fragments, then W
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
-        wf[bn] = *reinterpret_cast<const bf16x8*>(
-            sW + lds_off(wn * 128 + bn * 32 + frag_row, kk * 2 + frag_chunk));
+        for (int bm = 0; bm < 2; ++bm)
+          af[nb][bm] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 64 + bm * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-        af[bm] = *reinterpret_cast<const bf16x8*>(
-            sA + lds_off(wm * 64 + bm * 32 + frag_row, kk * 2 + frag_chunk));
+        for (int bn = 0; bn < 4; ++bn)
+          wf[nb][bn] = *reinterpret_cast<const bf16x8*>(sW + lds_off(wn * 128 + bn * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
+      }
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
         for (int bm = 0; bm < 2; ++bm)
-          acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[bn], af[bm], acc[bn][bm], 0, 0, 0);
+          acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][bn], af[cb][bm], acc[bn][bm], 0, 0, 0);
+      if (kk + 1 < BK / 16) {
+        // one fragment read between consecutive MFMAs
+        for (int i = 0; i < 6; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (kt + 1 < KT) BI_STORE_LDS(cur ^ 1);
     __syncthreads();
   }

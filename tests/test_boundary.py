@@ -106,13 +106,14 @@ SEQS = [dict(q_len=1, ctx_len=700, kv_base=0), dict(q_len=250, ctx_len=250, kv_b
 
 def test_step_pack_layout():
     n_tok = sum(s["q_len"] for s in SEQS)
-    nbytes = bi.lib().bi_step_meta_bytes(len(SEQS), n_tok)
-    buf = np.zeros(nbytes, np.uint8)
     arr = bi._seq_array(SEQS)
+    nbytes = bi.lib().bi_step_meta_bytes(arr, len(SEQS))
+    buf = np.zeros(nbytes, np.uint8)
     assert bi.lib().bi_step_pack(arr, len(SEQS), ctypes.c_void_p(buf.ctypes.data), nbytes - 1) == WS
     assert bi.lib().bi_step_pack(arr, len(SEQS), ctypes.c_void_p(buf.ctypes.data), nbytes) == OK
-    hdr = buf[:32].view(np.int64)
-    assert list(hdr) == [3, n_tok, 1, 2]
+    hdr = buf[:40].view(np.int64)
+    # 3 sequences, 252 tokens, 1 prefill, 2 decodes with 701 and 1 keys: 3 + 1 units
+    assert list(hdr) == [3, n_tok, 1, 2, 4]
     # prefill list at 256: {q_row, kv_base, q_start, q_len}
     pf = buf[256:256 + 24]
     assert pf[:16].view(np.int64).tolist() == [1, 1000] and pf[16:24].view(np.int32).tolist() == [250, 250]
@@ -127,6 +128,9 @@ def test_step_pack_layout():
     kv_off = pos_off + ((4 * n_tok + 255) // 256) * 256
     kvr = buf[kv_off:kv_off + 8 * n_tok].view(np.int64)
     assert kvr[0] == 700 and kvr[1] == 1250 and kvr[250] == 1499 and kvr[251] == 5000
+    u_off = kv_off + ((8 * n_tok + 255) // 256) * 256
+    units = buf[u_off:u_off + 32].view(np.int32).reshape(4, 2)
+    assert units.tolist() == [[0, 0], [0, 1], [0, 2], [1, 0]]
 
 
 def test_step_pack_rejects_bad_steps():
@@ -136,7 +140,7 @@ def test_step_pack_rejects_bad_steps():
                 [dict(q_len=1, ctx_len=0, kv_base=-5)]):
         assert L.bi_step_pack(bi._seq_array(bad), 1, ctypes.c_void_p(buf.ctypes.data), buf.size) == SHAPE
     assert L.bi_step_pack(bi._seq_array(SEQS), 0, ctypes.c_void_p(buf.ctypes.data), buf.size) == SHAPE
-    assert L.bi_step_meta_bytes(0, 10) == 0
+    assert L.bi_step_meta_bytes(bi._seq_array(SEQS), 0) == 0
 
 
 def test_block_workspace_layout():
