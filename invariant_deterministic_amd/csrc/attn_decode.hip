@@ -9,20 +9,20 @@
 // are merged in ascending s by a second kernel, so a request's bits never
 // depend on the batch, the other requests' lengths or the grid.
 //
-// Split kernel: one 256-thread work-group per (kv head g, unit s, request b)
+// Split kernel: one 512-thread work-group per (kv head g, unit s, request b)
 // (the block entry point passes a host-built list of the step's real units,
 // the standalone one launches the max-units grid and idle groups exit);
-// each wave owns 64 of the unit's keys.  For the G query heads sharing kv
-// head g:
+// For the G query heads sharing kv head g (8 waves, each owning 32 of the
+// unit's keys):
 //   scores  S^T = K Q^T on v_mfma_f32_16x16x32_bf16, the keys streamed from
 //           HBM straight into the MFMA operand layout (16 keys x 32 dims per
 //           operand, D/32 steps in ascending order), times scale * log2(e);
 //   m       exact maximum over the unit (order-free);
 //   p       exp2(score - m), staged in LDS; l = sum of p (fixed in-lane order,
-//           xor lanes 16 and 32, then waves 0..3);
+//           xor lanes 16 and 32, then waves 0..7);
 //   o       sum of p * v on the VALU: lane (key group kl, dims 8 dc..) walks
 //           its keys in ascending order with fmaf; the key groups of a wave
-//           are added by a fixed xor tree, the 4 waves in ascending order
+//           are added by a fixed xor tree, the 8 waves in ascending order
 //           through LDS.
 // Partials (m, l, o[D]) go to the workspace in fp32.  Keys past L_b are
 // neither loaded nor counted (score -inf, p = 0, value 0).
@@ -37,11 +37,14 @@ namespace bi {
 namespace {
 
 constexpr int kSplit = kKvSplit;      // 256 keys per unit
-constexpr int kWavesPerUnit = 4;      // 64 keys per wave
+constexpr int kWavesPerUnit = 8;      // 32 keys per wave
 constexpr int kKeysPerWave = kSplit / kWavesPerUnit;
 
+constexpr int kSplitThreads = 64 * kWavesPerUnit;
+constexpr int kKeyBlocks = kKeysPerWave / 16;  // 16-key MFMA blocks per wave
+
 template <int D, int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+__global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_all,
     const uint16_t* __restrict__ v_all, const DecodeSeq* __restrict__ seqs,
     const int2* __restrict__ units, int Hkv, int64_t max_len, int max_splits, float qscale,
@@ -78,9 +81,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   // A operand (keys): lane holds K[key_base + 16 kb + l16][32 ks + 8 grp .. + 8]
   // B operand (heads): lane holds Q[head l16][32 ks + 8 grp .. + 8] (0 past G)
   const uint16_t* kb_ptr = k_all + (sq.kv_offset + key_base + l16) * row_stride + g * D + grp * 8;
-  uint4 kr[4][KS];
+  uint4 kr[kKeyBlocks][KS];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < kKeyBlocks; ++kb) {
     const bool valid = key_base + 16 * kb + l16 < L;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -94,9 +97,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     if (l16 < G) v = *reinterpret_cast<const uint4*>(q + sq.q_row * q_stride + (g * G + l16) * D + 32 * ks + grp * 8);
     qb[ks] = as_bf16x8(v);
   }
-  f32x4 sacc[4];
+  f32x4 sacc[kKeyBlocks];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
+  for (int kb = 0; kb < kKeyBlocks; ++kb) {
     sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -114,10 +117,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
                                           : make_uint4(0, 0, 0, 0);
 
   // ---- scores: lane holds head l16, keys key_base + 16 kb + 4 grp + r
-  float sc[4][4];
+  float sc[kKeyBlocks][4];
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const bool valid = key_base + 16 * kb + 4 * grp + r < L;
@@ -130,10 +133,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   if (grp == 0 && l16 < G) s_m[w][l16] = mx;
   __syncthreads();
   const int hh = l16 < G ? l16 : 0;
-  const float m = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
+  float m = s_m[0][hh];
+#pragma unroll
+  for (int ww = 1; ww < kWavesPerUnit; ++ww) m = fmaxf(m, s_m[ww][hh]);
   float ls = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
+  for (int kb = 0; kb < kKeyBlocks; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float p = __builtin_amdgcn_exp2f(sc[kb][r] - m);
@@ -183,15 +188,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   __syncthreads();
 
   // ---- fixed-order sum over the waves; write the unit's partials
-  for (int i = threadIdx.x; i < G * D; i += 256) {
+  for (int i = threadIdx.x; i < G * D; i += kSplitThreads) {
     const int h = i / D;
     const int d = i % D;
-    const float o = ((s_o[0][h][d] + s_o[1][h][d]) + s_o[2][h][d]) + s_o[3][h][d];
+    float o = s_o[0][h][d];
+#pragma unroll
+    for (int ww = 1; ww < kWavesPerUnit; ++ww) o += s_o[ww][h][d];
     const int64_t slot = (int64_t(b) * Hq + g * G + h) * max_splits + s;
     ws_o[slot * D + d] = o;
     if (d == 0) {
-      ws_ml[slot * 2 + 0] = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
-      ws_ml[slot * 2 + 1] = ((s_l[0][h] + s_l[1][h]) + s_l[2][h]) + s_l[3][h];
+      float mm = s_m[0][h], ll = s_l[0][h];
+#pragma unroll
+      for (int ww = 1; ww < kWavesPerUnit; ++ww) {
+        mm = fmaxf(mm, s_m[ww][h]);
+        ll += s_l[ww][h];
+      }
+      ws_ml[slot * 2 + 0] = mm;
+      ws_ml[slot * 2 + 1] = ll;
     }
   }
 }
@@ -245,7 +258,7 @@ hipError_t launch_split(const uint16_t* q, int64_t q_stride, const uint16_t* k_a
                         int n_units, int B, int64_t max_len, int max_splits, int Hkv, float qscale,
                         float* ws_o, float* ws_ml, hipStream_t s) {
   const dim3 grid = units ? dim3(Hkv, n_units, 1) : dim3(Hkv, max_splits, B);
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(256), 0, s, q, q_stride, k_all,
+  hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(kSplitThreads), 0, s, q, q_stride, k_all,
                      v_all, seqs, units, Hkv, max_len, max_splits, qscale, ws_o, ws_ml);
   return hipGetLastError();
 }

@@ -30,7 +30,8 @@
 // Work-group = 8 waves = (kv head g, tile of P = 256 / G positions): wave w
 // takes query head g*G + w % G and the 32 positions tile + 32 (w / G).  The
 // waves share the K / V^T blocks in LDS (double-buffered through registers;
-// waves 0-3 move K, waves 4-7 move V and transpose it four keys at a time).
+// half the threads move K, the other half move V and transpose it 2 or 4 keys
+// at a time).  Tiles run longest first.
 #include "bi_dev.h"
 #include "bi_internal.h"
 
@@ -61,8 +62,9 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
   constexpr int DCH = D / 8;          // 16-byte chunks per row
   constexpr int KK = D / 16;          // MFMA k-steps for S
   constexpr int BD = D / 32;          // output blocks along D
-  constexpr int KPT = KB * DCH / 256; // K chunks (waves 0-3) / V keys (waves 4-7) per thread
-  static_assert(KPT == 2 || KPT == 4, "value transpose handles 2 or 4 keys per thread");
+  constexpr int HT = NTH / 2;         // threads moving K (first half) or V (second half)
+  constexpr int KPT = KB * DCH / HT;  // K chunks / V keys per thread
+  static_assert(KPT == 2 || KPT == 4 || KPT == 8, "value transpose handles 2, 4 or 8 keys per thread");
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][KB * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][KB * D];
 
@@ -105,12 +107,12 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     }
   }
 
-  // ---- block loads.  Waves 0-3 move K: thread u = t (0..255) takes chunk u %
-  // DCH of keys u / DCH + (256 / DCH) i.  Waves 4-7 move V: thread u = t - 256
-  // takes chunk u % DCH of the KPT consecutive keys KPT (u / DCH) .., which it
-  // transposes in registers into KPT-key rows of V^T.
-  const bool is_k = w < 4;
-  const int u = t & 255;
+  // ---- block loads.  The first half of the work-group moves K: thread u
+  // takes chunk u % DCH of keys u / DCH + (HT / DCH) i.  The second half moves
+  // V: thread u takes chunk u % DCH of the KPT consecutive keys KPT (u / DCH)
+  // .., which it transposes in registers into KPT-key rows of V^T.
+  const bool is_k = t < HT;
+  const int u = t % HT;
   const int uc = u % DCH;
   const int ur = u / DCH;
   const uint16_t* kbase = k_cache + sq.kv_base * kv_stride + int64_t(g) * D + uc * 8;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
   auto load_block = [&](int blk) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int key = blk * KB + (is_k ? ur + (256 / DCH) * i : KPT * ur + i);
+      const int key = blk * KB + (is_k ? ur + (HT / DCH) * i : KPT * ur + i);
       rr[i] = make_uint4(0, 0, 0, 0);
       if (key < kv_valid)
         rr[i] = *reinterpret_cast<const uint4*>((is_k ? kbase : vbase) + int64_t(key) * kv_stride);
@@ -129,24 +131,28 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     if (is_k) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i)
-        *reinterpret_cast<uint4*>(&sK[stage][k_off<D>(ur + (256 / DCH) * i, uc)]) = rr[i];
+        *reinterpret_cast<uint4*>(&sK[stage][k_off<D>(ur + (HT / DCH) * i, uc)]) = rr[i];
     } else {
       // rr[i] holds dims 8 uc .. + 8 of key KPT ur + i; row d of V^T gets the
-      // KPT keys' values of dim d (2 bytes each, ascending key).
+      // KPT keys' values of dim d (2 bytes each, ascending key), written as
+      // 8-byte granules of 4 keys.
       const uint32_t* w32 = reinterpret_cast<const uint32_t*>(rr);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = uc * 8 + e;
         // 16-bit element e of key i sits in word 4 i + e / 2, half e % 2
         const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        if constexpr (KPT == 4) {
-          uint2 v;
-          v.x = __builtin_amdgcn_perm(w32[4 + e / 2], w32[0 + e / 2], sel);
-          v.y = __builtin_amdgcn_perm(w32[12 + e / 2], w32[8 + e / 2], sel);
-          *reinterpret_cast<uint2*>(&sV[stage][vt_off(d, KPT * ur)]) = v;
+        if constexpr (KPT == 2) {
+          *reinterpret_cast<uint32_t*>(&sV[stage][vt_off(d, KPT * ur)]) =
+              __builtin_amdgcn_perm(w32[4 + e / 2], w32[0 + e / 2], sel);
         } else {
-          const uint32_t v = __builtin_amdgcn_perm(w32[4 + e / 2], w32[0 + e / 2], sel);
-          *reinterpret_cast<uint32_t*>(&sV[stage][vt_off(d, KPT * ur)]) = v;
+#pragma unroll
+          for (int q4 = 0; q4 < KPT / 4; ++q4) {
+            uint2 v;
+            v.x = __builtin_amdgcn_perm(w32[16 * q4 + 4 + e / 2], w32[16 * q4 + 0 + e / 2], sel);
+            v.y = __builtin_amdgcn_perm(w32[16 * q4 + 12 + e / 2], w32[16 * q4 + 8 + e / 2], sel);
+            *reinterpret_cast<uint2*>(&sV[stage][vt_off(d, KPT * ur + 4 * q4)]) = v;
+          }
         }
       }
     }
@@ -213,10 +219,13 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         }
       rs += __shfl_xor(rs, 32, 64);
       l_run = l_run * alpha + rs;
+      // multiplying by exactly 1 changes nothing: skip when no lane's max moved
+      if (__any(alpha != 1.0f)) {
 #pragma unroll
-      for (int bd = 0; bd < BD; ++bd)
+        for (int bd = 0; bd < BD; ++bd)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[bd][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc_o[bd][r] *= alpha;
+      }
       // O^T[d][q] += V^T[d][key] P^T[key][q].  P (fp32) enters the bf16 MFMA as
       // two bf16 terms, P = hi + lo with hi = bf16(P), lo = bf16(P - hi), so
       // the weights carry ~16 significant bits; each k-step adds V hi, then

@@ -31,6 +31,8 @@
 // A is the weight tile, operand B the activation tile, so each lane ends with
 // 4 consecutive output columns of one output row and stores them as one
 // 8-byte write.
+#include <type_traits>
+
 #include "bi_dev.h"
 #include "bi_internal.h"
 
@@ -153,21 +155,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bn][bm][r] = 0.f;
 
-  const int KT = K / BK;
-  BI_LOAD_GLOBAL(0);
-  BI_STORE_LDS(0);
-  __syncthreads();
-
   const int frag_row = lane & 31;
   const int frag_chunk = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) BI_LOAD_GLOBAL(kt + 1);
-    const uint16_t* sA = smem[cur][0];
-    const uint16_t* sW = smem[cur][1];
-    bf16x8 wf[2][4], af[2][2];
+  // MFMA work of one stage for the wave's first NBM 32-row blocks.  Blocks
+  // that lie entirely past M are skipped: that removes only padding work and
+  // leaves every valid element's instruction sequence unchanged.
+  const int wave_row0 = tm * BM + wm * 64;
+  const int nbm = wave_row0 >= M ? 0 : (wave_row0 + 32 >= M ? 1 : 2);
+  auto compute_stage = [&](const uint16_t* sA, const uint16_t* sW, auto nbm_c) {
+    constexpr int NBM = decltype(nbm_c)::value;
+    bf16x8 wf[2][4], af[2][NBM];
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
+    for (int bm = 0; bm < NBM; ++bm)
       af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 64 + bm * 32 + frag_row, frag_chunk));
 #pragma unroll
     for (int bn = 0; bn < 4; ++bn)
@@ -179,7 +178,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
       if (kk + 1 < BK / 16) {
         // read in the order the next substep uses them: A fragments, then W
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
+        for (int bm = 0; bm < NBM; ++bm)
           af[nb][bm] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 64 + bm * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
 #pragma unroll
         for (int bn = 0; bn < 4; ++bn)
@@ -188,18 +187,33 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn)
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm)
+        for (int bm = 0; bm < NBM; ++bm)
           acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][bn], af[cb][bm], acc[bn][bm], 0, 0, 0);
       if (kk + 1 < BK / 16) {
         // one fragment read between consecutive MFMAs
-        for (int i = 0; i < 6; ++i) {
+#pragma unroll
+        for (int i = 0; i < NBM + 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if constexpr (4 * NBM > NBM + 4) __builtin_amdgcn_sched_group_barrier(0x008, 4 * NBM - NBM - 4, 0);
       }
     }
     __builtin_amdgcn_s_setprio(0);
+  };
+
+  const int KT = K / BK;
+  BI_LOAD_GLOBAL(0);
+  BI_STORE_LDS(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < KT) BI_LOAD_GLOBAL(kt + 1);
+    const uint16_t* sA = smem[cur][0];
+    const uint16_t* sW = smem[cur][1];
+    if (nbm == 2) compute_stage(sA, sW, std::integral_constant<int, 2>{});
+    else if (nbm == 1) compute_stage(sA, sW, std::integral_constant<int, 1>{});
     if (kt + 1 < KT) BI_STORE_LDS(cur ^ 1);
     __syncthreads();
   }
