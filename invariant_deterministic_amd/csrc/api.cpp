@@ -58,6 +58,8 @@ bool head_shape_ok(int Hq, int Hkv, int D, int max_group) {
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return false;
   if (G > max_group) return false;
+  // a 256-key unit of one kv head is addressed with 32-bit buffer offsets
+  if (int64_t(Hkv) * D > 65536) return false;
   return D == 64 || D == 128;
 }
 

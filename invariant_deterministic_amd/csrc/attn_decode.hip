@@ -11,21 +11,26 @@
 //
 // Split kernel: one 512-thread work-group per (kv head g, unit s, request b)
 // (the block entry point passes a host-built list of the step's real units,
-// the standalone one launches the max-units grid and idle groups exit);
-// For the G query heads sharing kv head g (8 waves, each owning 32 of the
-// unit's keys):
-//   scores  S^T = K Q^T on v_mfma_f32_16x16x32_bf16, the keys streamed from
-//           HBM straight into the MFMA operand layout (16 keys x 32 dims per
-//           operand, D/32 steps in ascending order), times scale * log2(e);
+// the standalone one launches the max-units grid and idle groups exit), for
+// the G query heads sharing kv head g; 8 waves, each owning 32 of the keys.
+//   loads   token-major: a lane takes 16 bytes (D/16 dims) of one key row, so
+//           each load instruction covers four whole head rows; raw buffer
+//           loads bounded at the request's last key read zero past it, with no
+//           branch.  The query rows go once through LDS.
+//   scores  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (D/32 k-steps in ascending
+//           order), K passed through a per-wave LDS block of 16 keys to reach
+//           the operand layout, times scale * log2(e).  The block's row order
+//           is chosen so that each lane ends up holding the scores of the very
+//           keys whose values it loaded.
 //   m       exact maximum over the unit (order-free);
-//   p       exp2(score - m), staged in LDS; l = sum of p (fixed in-lane order,
-//           xor lanes 16 and 32, then waves 0..7);
-//   o       sum of p * v on the VALU: lane (key group kl, dims 8 dc..) walks
-//           its keys in ascending order with fmaf; the key groups of a wave
-//           are added by a fixed xor tree, the 8 waves in ascending order
-//           through LDS.
-// Partials (m, l, o[D]) go to the workspace in fp32.  Keys past L_b are
-// neither loaded nor counted (score -inf, p = 0, value 0).
+//   p       exp2(score - m); l = sum of p (fixed in-lane order, lane pairs
+//           16 and 32 apart, then waves 0..7);
+//   o       P V on v_mfma_f32_16x16x32_bf16: the value operand is the lane's own
+//           token-major registers regrouped by byte permutes (eight keys of one
+//           dim), P enters as a bf16 high part plus a bf16 remainder; the 8
+//           waves' partials are added in ascending order through LDS.
+// Partials (m, l, o[D]) go to the workspace in fp32.  Keys past L_b contribute
+// score -inf, p = 0 and value 0.
 //
 // Combine kernel: one thread per (request, head, dim) walks s = 0 .. S_b - 1
 // in ascending order: M = max m_s; w_s = exp2(m_s - M); O = sum w_s o_s,
@@ -39,9 +44,7 @@ namespace {
 constexpr int kSplit = kKvSplit;      // 256 keys per unit
 constexpr int kWavesPerUnit = 8;      // 32 keys per wave
 constexpr int kKeysPerWave = kSplit / kWavesPerUnit;
-
 constexpr int kSplitThreads = 64 * kWavesPerUnit;
-constexpr int kKeyBlocks = kKeysPerWave / 16;  // 16-key MFMA blocks per wave
 
 template <int D, int G>
 __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(
@@ -49,15 +52,20 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(
     const uint16_t* __restrict__ v_all, const DecodeSeq* __restrict__ seqs,
     const int2* __restrict__ units, int Hkv, int64_t max_len, int max_splits, float qscale,
     float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  constexpr int KS = D / 32;     // MFMA k-steps over the head dimension
-  constexpr int CH = D / 8;      // lanes per key row in the value pass
-  constexpr int KPL = 64 / CH;   // keys per wave-wide value load
-  constexpr int NIT = kKeysPerWave / KPL;
-  static_assert(G <= 16, "one 16-wide MFMA column block holds the group's heads");
+  constexpr int LD = D / 16;              // dims per lane in the token-major loads
+  constexpr int NDW = LD / 2;             // their dwords
+  constexpr int KS = D / 32;              // MFMA k-steps over the head dimension
+  constexpr int NG = D / 8;               // 16-byte granules per key row
+  constexpr int NIT = kKeysPerWave / 4;   // lane keys: 4 it + grp
+  constexpr int NKB = kKeysPerWave / 16;  // 16-key score blocks
+  constexpr int NKS = kKeysPerWave / 32;  // 32-key value steps
+  static_assert(kKeysPerWave % 32 == 0 && G <= 8, "whole value steps; a wave's partial fits its key buffer");
+  // per wave: one 16-key block of K (row-major, 16-byte granules xor-swizzled
+  // by the row), later the wave's partial o[G][D] in fp32
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[kWavesPerUnit][16 * D];
   __shared__ float s_m[kWavesPerUnit][G];
   __shared__ float s_l[kWavesPerUnit][G];
-  __shared__ __attribute__((aligned(16))) float s_p[kWavesPerUnit][kKeysPerWave][G];
-  __shared__ float s_o[kWavesPerUnit][G][D];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[G * D];  // the G query heads
 
   const int g = blockIdx.x;   // kv heads of one key block are dispatched together
   // (request, unit) from a host-built list of real units, or the full grid
@@ -77,113 +85,129 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(
   const int64_t row_stride = int64_t(Hkv) * D;
   const int64_t key_base = int64_t(s) * kSplit + w * kKeysPerWave;
 
-  // ---- S^T = K Q^T with v_mfma_f32_16x16x32_bf16, straight from HBM.
-  // A operand (keys): lane holds K[key_base + 16 kb + l16][32 ks + 8 grp .. + 8]
-  // B operand (heads): lane holds Q[head l16][32 ks + 8 grp .. + 8] (0 past G)
-  const uint16_t* kb_ptr = k_all + (sq.kv_offset + key_base + l16) * row_stride + g * D + grp * 8;
-  uint4 kr[kKeyBlocks][KS];
+  // ---- loads.  Query: the G rows of this kv head, 16 bytes per thread.
+  const bool q_thread = threadIdx.x < G * D / 8;
+  uint32_t qv[4];
+  buf_ld_stream<4>(buf_rsrc(q + sq.q_row * q_stride + g * G * D, G * D * 2), threadIdx.x * 16, qv);
+  // Keys and values: lane (grp, l16) takes dims LD l16 .. + LD of keys
+  // key_base + 4 it + grp; the buffers end at the unit's last valid key.
+  const int64_t left = L - int64_t(s) * kSplit;
+  const uint32_t nv = uint32_t(left < kSplit ? left : kSplit);
+  const uint32_t row_bytes = uint32_t(row_stride) * 2;
+  const int64_t unit_row = sq.kv_offset + int64_t(s) * kSplit;
+  const __amdgpu_buffer_rsrc_t krs = buf_rsrc(k_all + unit_row * row_stride + g * D, nv * row_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(v_all + unit_row * row_stride + g * D, nv * row_bytes);
+  const uint32_t lane_off = uint32_t(w * kKeysPerWave + grp) * row_bytes + uint32_t(l16) * LD * 2;
+  uint32_t kw[NIT][NDW], vw[NIT][NDW];
 #pragma unroll
-  for (int kb = 0; kb < kKeyBlocks; ++kb) {
-    const bool valid = key_base + 16 * kb + l16 < L;
+  for (int it = 0; it < NIT; ++it) buf_ld_stream<NDW>(krs, lane_off + uint32_t(4 * it) * row_bytes, kw[it]);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kr[kb][ks] = valid ? ld_stream16(kb_ptr + int64_t(16 * kb) * row_stride + 32 * ks)
-                         : make_uint4(0, 0, 0, 0);
-  }
-  bf16x8 qb[KS];
+  for (int it = 0; it < NIT; ++it) buf_ld_stream<NDW>(vrs, lane_off + uint32_t(4 * it) * row_bytes, vw[it]);
+  if (q_thread) *reinterpret_cast<uint4*>(s_q + threadIdx.x * 8) = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+  __syncthreads();
+
+  // ---- S^T = K Q^T, one 16-key block kb at a time through the wave's LDS
+  // buffer.  Block row i holds wave key 16 kb + 4 (i & 3) + (i >> 2), so output
+  // register r of lane (head l16, grp) is the score of key 4 (4 kb + r) + grp:
+  // the keys of the lane's own value registers.
+  uint16_t* sk = s_k[w];
+  f32x4 sacc[NKB];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (l16 < G) v = *reinterpret_cast<const uint4*>(q + sq.q_row * q_stride + (g * G + l16) * D + 32 * ks + grp * 8);
-    qb[ks] = as_bf16x8(v);
-  }
-  f32x4 sacc[kKeyBlocks];
+  for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-  for (int kb = 0; kb < kKeyBlocks; ++kb) {
+    for (int j = 0; j < 4; ++j) {
+      const int kr = 4 * j + grp;  // key row within the block
+      const uint32_t* src = kw[4 * kb + j];
+      if constexpr (NDW == 4) {
+        const int phys = l16 ^ (kr & (NG - 1));
+        *reinterpret_cast<uint4*>(sk + kr * D + phys * 8) = make_uint4(src[0], src[1], src[2], src[3]);
+      } else {
+        const int phys = (l16 >> 1) ^ (kr & (NG - 1));
+        *reinterpret_cast<uint2*>(sk + kr * D + phys * 8 + (l16 & 1) * 4) = make_uint2(src[0], src[1]);
+      }
+    }
+    const int rr = 4 * (l16 & 3) + (l16 >> 2);
     sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[kb][ks]), qb[ks], sacc[kb], 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks) {
+      // A operand: K[row rr][32 ks + 8 grp .. + 8]; B operand: Q[head l16][same dims] (0 past G)
+      const int phys = (4 * ks + grp) ^ (rr & (NG - 1));
+      const uint4 a = *reinterpret_cast<const uint4*>(sk + rr * D + phys * 8);
+      const uint4 qq = l16 < G ? *reinterpret_cast<const uint4*>(s_q + l16 * D + 32 * ks + 8 * grp)
+                               : make_uint4(0, 0, 0, 0);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qq), sacc[kb], 0, 0, 0);
+    }
   }
 
-  // value loads go out now; their latency overlaps the softmax
-  const int dc = lane % CH;
-  const int kl = lane / CH;
-  const uint16_t* vb_ptr = v_all + (sq.kv_offset + key_base + kl) * row_stride + g * D + dc * 8;
-  uint4 vr[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it)
-    vr[it] = key_base + it * KPL + kl < L ? ld_stream16(vb_ptr + int64_t(it * KPL) * row_stride)
-                                          : make_uint4(0, 0, 0, 0);
-
-  // ---- scores: lane holds head l16, keys key_base + 16 kb + 4 grp + r
-  float sc[kKeyBlocks][4];
+  // ---- softmax over the unit: lane holds head l16, keys key_base + 4 it + grp
+  float sc[NIT];
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < kKeyBlocks; ++kb)
+  for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const bool valid = key_base + 16 * kb + 4 * grp + r < L;
+      const int it = 4 * kb + r;
+      const bool valid = key_base + 4 * it + grp < L;
       const float v = valid ? sacc[kb][r] * qscale : -INFINITY;
-      sc[kb][r] = v;
+      sc[it] = v;
       mx = fmaxf(mx, v);
     }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  mx = max_x32(max_x16(mx));
   if (grp == 0 && l16 < G) s_m[w][l16] = mx;
   __syncthreads();
   const int hh = l16 < G ? l16 : 0;
   float m = s_m[0][hh];
 #pragma unroll
   for (int ww = 1; ww < kWavesPerUnit; ++ww) m = fmaxf(m, s_m[ww][hh]);
+  float p[NIT];
   float ls = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < kKeyBlocks; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = __builtin_amdgcn_exp2f(sc[kb][r] - m);
-      ls += p;
-      if (l16 < G) s_p[w][16 * kb + 4 * grp + r][l16] = p;
-    }
-  ls += __shfl_xor(ls, 16, 64);
-  ls += __shfl_xor(ls, 32, 64);
-  if (grp == 0 && l16 < G) s_l[w][l16] = ls;
-  __syncthreads();
-
-  // ---- weighted values: lane takes dims 8 dc .. + 8 of keys kl, kl + KPL, ...
-  float oacc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) oacc[h][e] = 0.f;
-#pragma unroll
   for (int it = 0; it < NIT; ++it) {
-    float vf[8];
-    unpack8(vr[it], vf);
-    const float* pp = s_p[w][it * KPL + kl];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float p = pp[h];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) oacc[h][e] = __builtin_fmaf(p, vf[e], oacc[h][e]);
-    }
+    p[it] = l16 < G ? __builtin_amdgcn_exp2f(sc[it] - m) : 0.f;
+    ls += p[it];
   }
-  // key groups of the wave (lanes with equal dc) by a fixed xor tree, then
-  // one partial per wave through LDS
+  ls = sum_x32(sum_x16(ls));
+  if (grp == 0 && l16 < G) s_l[w][l16] = ls;
+  // P as a bf16 high part plus a bf16 remainder (A operand: row head l16,
+  // k = it of the lane's key group)
+  uint4 ph[NKS], pl[NKS];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int kk = 0; kk < NKS; ++kk) {
+    uint32_t h4[4], l4[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = oacc[h][e];
-#pragma unroll
-      for (int off = CH; off < 64; off <<= 1) v += __shfl_xor(v, off, 64);
-      oacc[h][e] = v;
+    for (int j = 0; j < 4; ++j) {
+      const float p0 = p[8 * kk + 2 * j], p1 = p[8 * kk + 2 * j + 1];
+      const uint16_t a = f2bf(p0), c = f2bf(p1);
+      h4[j] = uint32_t(a) | (uint32_t(c) << 16);
+      l4[j] = pack2bf(p0 - bf2f(a), p1 - bf2f(c));
     }
-  if (kl == 0) {
+    ph[kk] = make_uint4(h4[0], h4[1], h4[2], h4[3]);
+    pl[kk] = make_uint4(l4[0], l4[1], l4[2], l4[3]);
+  }
+
+  // ---- O = P V, one MFMA block per lane dim e: B operand lane (col l16, grp)
+  // holds V[key 4 it + grp][dim LD l16 + e], it = 8 kk .. 8 kk + 7, regrouped
+  // from the token-major registers by byte permutes.  Lane (l16, grp) gets
+  // heads 4 grp + r of dim LD l16 + e; the wave's partial goes into its own
+  // (now free) key buffer.
+  float* so = reinterpret_cast<float*>(sk);
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+  for (int e = 0; e < LD; ++e) {
+    f32x4 oacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[w][h][dc * 8 + e] = oacc[h][e];
+    for (int kk = 0; kk < NKS; ++kk) {
+      uint32_t vt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vt[j] = __builtin_amdgcn_perm(vw[8 * kk + 2 * j + 1][e >> 1], vw[8 * kk + 2 * j][e >> 1],
+                                      (e & 1) ? 0x07060302u : 0x05040100u);
+      const bf16x8 vb = as_bf16x8(make_uint4(vt[0], vt[1], vt[2], vt[3]));
+      oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ph[kk]), vb, oacc, 0, 0, 0);
+      oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pl[kk]), vb, oacc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * grp + r < G) so[(4 * grp + r) * D + LD * l16 + e] = oacc[r];
   }
   __syncthreads();
 
@@ -191,9 +215,9 @@ __global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(
   for (int i = threadIdx.x; i < G * D; i += kSplitThreads) {
     const int h = i / D;
     const int d = i % D;
-    float o = s_o[0][h][d];
+    float o = reinterpret_cast<const float*>(s_k[0])[h * D + d];
 #pragma unroll
-    for (int ww = 1; ww < kWavesPerUnit; ++ww) o += s_o[ww][h][d];
+    for (int ww = 1; ww < kWavesPerUnit; ++ww) o += reinterpret_cast<const float*>(s_k[ww])[h * D + d];
     const int64_t slot = (int64_t(b) * Hq + g * G + h) * max_splits + s;
     ws_o[slot * D + d] = o;
     if (d == 0) {

@@ -76,4 +76,44 @@ __device__ __forceinline__ float xor_max(float v) {
   return v;
 }
 
+// Lane-pair exchanges without LDS (v_permlane16_swap / v_permlane32_swap).
+// pswap16(a, b): within each 32-lane half, the odd 16-lane row of a trades
+// places with the even row of b; pswap32(a, b): the upper 32 lanes of a trade
+// places with the lower 32 lanes of b.  With a == b, a op b afterwards combines
+// lanes l and l ^ 16 (l ^ 32) -- for a commutative op every lane of the pair
+// gets the same bits.
+__device__ __forceinline__ void pswap16(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pswap32(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x16(float x) { float y = x; pswap16(x, y); return x + y; }
+__device__ __forceinline__ float sum_x32(float x) { float y = x; pswap32(x, y); return x + y; }
+__device__ __forceinline__ float max_x16(float x) { float y = x; pswap16(x, y); return fmaxf(x, y); }
+__device__ __forceinline__ float max_x32(float x) { float y = x; pswap32(x, y); return fmaxf(x, y); }
+
+// Raw buffer resource over `bytes` bytes at p.  Loads through it at byte
+// offsets >= bytes return zero and touch no memory, so a tile's ragged edge
+// needs no branch (a branch around a load can cost a full-latency wait).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, int(bytes), 0x00020000);
+}
+// NDW (4 or 2) dwords at byte offset off, streamed past the caches.
+template <int NDW>
+__device__ __forceinline__ void buf_ld_stream(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* out) {
+  if constexpr (NDW == 4) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 2);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  } else {
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, int(off), 0, 2);
+    out[0] = v.x; out[1] = v.y;
+  }
+}
+
 }  // namespace bi
