@@ -23,8 +23,11 @@
 // bit-identical to the bf16 GEMM on the de-quantised weight.
 //
 // Data flow: global -> registers (prefetch of step k+1 during step k) -> LDS
-// (two stages, 16-byte chunks xor-swizzled by row to keep ds_read_b128
-// conflict-free) -> MFMA operands.  Inside a step the fragments of k-substep
+// (two stages, 16-byte chunks xor-swizzled by row pair to keep ds_read_b128
+// and ds_write_b128 conflict-free) -> MFMA operands.  Step k+1's registers go
+// into the free LDS stage in the middle of step k's MFMA stream (after its
+// third substep), so the stores and their wait for the global loads overlap
+// the matrix work; one barrier per step.  Inside a step the fragments of k-substep
 // kk+1 are read while the MFMAs of kk run, one LDS read between consecutive
 // MFMAs (scheduling hints), and the MFMA phase runs at raised wave priority
 // so the SIMD's other wave issues its memory work in the gaps.  MFMA operand
@@ -42,11 +45,16 @@ namespace {
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
 constexpr int NT = 512;                 // 8 waves: 2 along N (128 each) x 4 along M (64 each)
 constexpr int TILE = BM * BK;           // bf16 elements of one operand tile (BM == BN)
+constexpr int kStoreAfter = 2;         // the next stage is written to LDS after this substep's MFMAs
 static_assert(BM == BN, "square tile assumed by the LDS layout");
 
-// Element offset of 16-byte chunk `chunk` (0..7) of tile row `row`.
+// Element offset of 16-byte chunk `chunk` (0..7) of tile row `row`.  LDS
+// serves 16 lanes of a 16-byte access per cycle from 64 four-byte banks, i.e.
+// two 128-byte rows; keying the xor on row / 2 puts the 16 rows a fragment
+// read touches per cycle (and the two rows a tile store touches) on 16
+// distinct 16-byte bank groups.
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * BK + ((chunk ^ (row & 7)) << 3);
+  return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
 // Expand one int4 group (16 bytes = 32 codes, one fp16 scale) into four
@@ -159,47 +167,58 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
   const int frag_chunk = lane >> 5;
   // MFMA work of one stage for the wave's first NBM 32-row blocks.  Blocks
   // that lie entirely past M are skipped: that removes only padding work and
-  // leaves every valid element's instruction sequence unchanged.
+  // leaves every valid element's instruction sequence unchanged.  A wave with
+  // no block left still loads and stores its share of every tile and meets
+  // every barrier.  `store` (the next stage's LDS writes) runs after the MFMAs
+  // of substep SAT (-1: no store).
   const int wave_row0 = tm * BM + wm * 64;
   const int nbm = wave_row0 >= M ? 0 : (wave_row0 + 32 >= M ? 1 : 2);
-  auto compute_stage = [&](const uint16_t* sA, const uint16_t* sW, auto nbm_c) {
+  auto compute_stage = [&](const uint16_t* sA, const uint16_t* sW, auto nbm_c, auto store_c, auto&& store) {
     constexpr int NBM = decltype(nbm_c)::value;
-    bf16x8 wf[2][4], af[2][NBM];
+    constexpr int SAT = decltype(store_c)::value;
+    if constexpr (NBM == 0) {
+      if constexpr (SAT >= 0) store();
+    } else {
+      bf16x8 wf[2][4], af[2][NBM];
 #pragma unroll
-    for (int bm = 0; bm < NBM; ++bm)
-      af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 64 + bm * 32 + frag_row, frag_chunk));
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn)
-      wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + lds_off(wn * 128 + bn * 32 + frag_row, frag_chunk));
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      const int cb = kk & 1, nb = cb ^ 1;
-      if (kk + 1 < BK / 16) {
-        // read in the order the next substep uses them: A fragments, then W
-#pragma unroll
-        for (int bm = 0; bm < NBM; ++bm)
-          af[nb][bm] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 64 + bm * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
-#pragma unroll
-        for (int bn = 0; bn < 4; ++bn)
-          wf[nb][bn] = *reinterpret_cast<const bf16x8*>(sW + lds_off(wn * 128 + bn * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
-      }
+      for (int bm = 0; bm < NBM; ++bm)
+        af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 64 + bm * 32 + frag_row, frag_chunk));
 #pragma unroll
       for (int bn = 0; bn < 4; ++bn)
+        wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + lds_off(wn * 128 + bn * 32 + frag_row, frag_chunk));
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int bm = 0; bm < NBM; ++bm)
-          acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][bn], af[cb][bm], acc[bn][bm], 0, 0, 0);
-      if (kk + 1 < BK / 16) {
-        // one fragment read between consecutive MFMAs
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        const int cb = kk & 1, nb = cb ^ 1;
+        if (kk + 1 < BK / 16) {
+          // read in the order the next substep uses them: A fragments, then W
 #pragma unroll
-        for (int i = 0; i < NBM + 4; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          for (int bm = 0; bm < NBM; ++bm)
+            af[nb][bm] = *reinterpret_cast<const bf16x8*>(
+                sA + lds_off(wm * 64 + bm * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
+#pragma unroll
+          for (int bn = 0; bn < 4; ++bn)
+            wf[nb][bn] = *reinterpret_cast<const bf16x8*>(
+                sW + lds_off(wn * 128 + bn * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
         }
-        if constexpr (4 * NBM > NBM + 4) __builtin_amdgcn_sched_group_barrier(0x008, 4 * NBM - NBM - 4, 0);
+#pragma unroll
+        for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+          for (int bm = 0; bm < NBM; ++bm)
+            acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][bn], af[cb][bm], acc[bn][bm], 0, 0, 0);
+        if (kk == SAT) store();
+        if (kk + 1 < BK / 16) {
+          // one fragment read between consecutive MFMAs
+#pragma unroll
+          for (int i = 0; i < NBM + 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          if constexpr (4 * NBM > NBM + 4) __builtin_amdgcn_sched_group_barrier(0x008, 4 * NBM - NBM - 4, 0);
+        }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
-    __builtin_amdgcn_s_setprio(0);
   };
 
   const int KT = K / BK;
@@ -207,16 +226,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
   BI_STORE_LDS(0);
   __syncthreads();
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) BI_LOAD_GLOBAL(kt + 1);
-    const uint16_t* sA = smem[cur][0];
-    const uint16_t* sW = smem[cur][1];
-    if (nbm == 2) compute_stage(sA, sW, std::integral_constant<int, 2>{});
-    else if (nbm == 1) compute_stage(sA, sW, std::integral_constant<int, 1>{});
-    if (kt + 1 < KT) BI_STORE_LDS(cur ^ 1);
-    __syncthreads();
-  }
+  auto run = [&](auto nbm_c) {
+    for (int kt = 0; kt + 1 < KT; ++kt) {
+      const int cur = kt & 1;
+      BI_LOAD_GLOBAL(kt + 1);
+      compute_stage(smem[cur][0], smem[cur][1], nbm_c, std::integral_constant<int, kStoreAfter>{},
+                    [&] { BI_STORE_LDS(cur ^ 1); });
+      __syncthreads();
+    }
+    const int cur = (KT - 1) & 1;
+    compute_stage(smem[cur][0], smem[cur][1], nbm_c, std::integral_constant<int, -1>{}, [] {});
+  };
+  if (nbm == 2) run(std::integral_constant<int, 2>{});
+  else if (nbm == 1) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
 
   // ---- epilogue: acc[bn][bm][r] is C[m][n] with
   //   m = tile row base + wm*64 + bm*32 + (lane & 31)
@@ -268,3 +291,4 @@ hipError_t launch_gemm_w4(const uint16_t* A, const uint8_t* Wq, const uint16_t* 
 }
 
 }  // namespace bi
+
