@@ -18,7 +18,8 @@
 //    lies wholly after the wave's queries is skipped).
 //  * Rows of a tile outside the chunk (before its first position or after its
 //    last) are computed with zero queries and never stored; keys at or after
-//    the end of the chunk are not read (zero in LDS) and are always masked.
+//    the end of the chunk read as zero (bounded buffer loads, no branch) and
+//    are always masked.
 //
 // Per wave and block (D = head_dim, G = query heads per kv head), for the
 // wave's 32 keys:
@@ -104,16 +105,23 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
   const int u = t % HT;
   const int uc = u % DCH;
   const int ur = u / DCH;
-  const uint16_t* kbase = k_cache + sq.kv_base * kv_stride + int64_t(g) * D + uc * 8;
-  const uint16_t* vbase = v_cache + sq.kv_base * kv_stride + int64_t(g) * D + uc * 8;
+  // head g's slice of the sequence's cache rows; the lane's 16-byte chunk uc
+  // goes into the per-lane buffer offset
+  const uint16_t* kbase = k_cache + sq.kv_base * kv_stride + int64_t(g) * D;
+  const uint16_t* vbase = v_cache + sq.kv_base * kv_stride + int64_t(g) * D;
   uint4 rr[KPT];
+  // block blk as a buffer over its valid keys (keys >= kv_valid read as zero)
   auto load_block = [&](int blk) {
+    const int nvalid = min(KB, max(0, kv_valid - blk * KB));
+    // K or V is chosen per wave (the first HT threads move K)
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(wave_uniform((is_k ? kbase : vbase) + int64_t(blk) * KB * kv_stride),
+                                               wave_uniform(uint32_t(nvalid) * uint32_t(kv_stride) * 2));
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int key = blk * KB + (is_k ? ur + (HT / DCH) * i : KPT * ur + i);
-      rr[i] = make_uint4(0, 0, 0, 0);
-      if (key < kv_valid)
-        rr[i] = *reinterpret_cast<const uint4*>((is_k ? kbase : vbase) + int64_t(key) * kv_stride);
+      const int key = is_k ? ur + (HT / DCH) * i : KPT * ur + i;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, int(uint32_t(key) * uint32_t(kv_stride) * 2 + uint32_t(uc) * 16), 0, 0);
+      rr[i] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
   auto store_block = [&](int stage) {
@@ -155,15 +163,23 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     // queries: B operand of S^T = K Q^T, lane holds Q[pos = wpos + l32][dims (2 kk + hf) * 8 .. + 8]
     bf16x8 qf[KK];
     {
+      // rows of the chunk as a buffer: positions outside it read as zero
       const int pos = wpos + l32;
-      const bool in = pos >= sq.q_start && pos <= last_pos;
-      const uint16_t* src = q + (sq.q_row + (pos - sq.q_start)) * q_stride + h * D + hf * 8;
+      const int r0 = wpos - sq.q_start;  // chunk row of the wave's first position (may be negative)
+      const int lo = max(r0, 0), hi = min(r0 + QW, sq.q_len);
+      const uint32_t nrows = hi > lo ? uint32_t(hi - lo) : 0u;
+      const __amdgpu_buffer_rsrc_t rs =
+          buf_rsrc(wave_uniform(q + (sq.q_row + lo) * q_stride + h * D), wave_uniform(nrows * uint32_t(q_stride) * 2));
+      // lanes before the chunk get an offset past the buffer's end
+      const uint32_t row_off = pos - sq.q_start >= lo ? uint32_t(pos - sq.q_start - lo) : nrows;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (in) v = *reinterpret_cast<const uint4*>(src + kk * 16);
-        qf[kk] = as_bf16x8(v);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, int(row_off * uint32_t(q_stride) * 2 + uint32_t(hf * 8 + kk * 16) * 2), 0, 0);
+        qf[kk] = as_bf16x8(make_uint4(v.x, v.y, v.z, v.w));
       }
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qf[kk]));  // complete before the block loop
     }
     f32x16 acc_o[BD];
 #pragma unroll
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     __syncthreads();
     for (int blk = 0; blk < n_blk; ++blk) {
       const int cur = blk & 1;
-      if (blk + 1 < n_blk) load_block(blk + 1);
+      load_block(blk + 1 < n_blk ? blk + 1 : blk);  // the last step reloads its own block (unused)
       if (wave_active && blk < wave_end_blk) {
         const uint16_t* cK = sKV[0][cur];
         const uint16_t* cV = sKV[1][cur];
@@ -348,4 +364,5 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t q_row_stride, const ui
 }
 
 }  // namespace bi
+
 

@@ -116,4 +116,14 @@ __device__ __forceinline__ void buf_ld_stream(__amdgpu_buffer_rsrc_t r, uint32_t
   }
 }
 
+// A value the caller knows is the same in every lane of the wave, moved to a
+// scalar register (buffer resources must be scalar).
+__device__ __forceinline__ const uint16_t* wave_uniform(const uint16_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const uint16_t*>((uint64_t(hi) << 32) | lo);
+}
+__device__ __forceinline__ uint32_t wave_uniform(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
 }  // namespace bi
