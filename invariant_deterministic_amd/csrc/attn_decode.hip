@@ -250,9 +250,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   }
   const int S = int((L + kSplit - 1) / kSplit);
   const int64_t base = (int64_t(b) * Hq + h) * max_splits;
+  // (unrolled so several units' loads are in flight; the sums stay in
+  // ascending s)
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) M = fmaxf(M, ws_ml[(base + s) * 2]);
   float Lsum = 0.f, O = 0.f;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) {
     const float w = __builtin_amdgcn_exp2f(ws_ml[(base + s) * 2] - M);
     Lsum = __builtin_fmaf(w, ws_ml[(base + s) * 2 + 1], Lsum);

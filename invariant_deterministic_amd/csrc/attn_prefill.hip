@@ -238,6 +238,8 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_o[bd][r] *= alpha;
         }
+        // the next block goes into the free stage here, overlapping the PV MFMAs
+        if (blk + 1 < n_blk) store_block(cur ^ 1);
         // O^T[d][q] += V^T[d][key] P^T[key][q], P = hi + lo in bf16; MFMA
         // k-slot hf*8 + e of step `half` is key 32 kh + 16 half + 8 (e / 4) +
         // 4 hf + e % 4 = register 8 half + e of S^T.
@@ -266,7 +268,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
           }
         }
       }
-      if (blk + 1 < n_blk) store_block(cur ^ 1);
+      if (!(wave_active && blk < wave_end_blk) && blk + 1 < n_blk) store_block(cur ^ 1);  // idle waves
       __syncthreads();
     }
 
@@ -364,5 +366,6 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t q_row_stride, const ui
 }
 
 }  // namespace bi
+
 
 
