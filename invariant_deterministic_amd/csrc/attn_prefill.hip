@@ -53,14 +53,21 @@ constexpr int QW = 32;                // query positions per wave
 constexpr int NW = 8;                 // waves per work-group
 constexpr int NTH = NW * 64;
 
-// K block in LDS: [64 keys][D], 16-byte chunks xor-swizzled by key.
+// K block in LDS: [64 keys][D], 16-byte chunks xor-swizzled by key so that
+// the 16 keys one 16-lane cycle of a fragment read touches sit on 16 distinct
+// 16-byte bank groups (64 four-byte banks = 256 bytes: one D = 128 row, two
+// D = 64 rows).
 template <int D>
 __device__ __forceinline__ int k_off(int key, int chunk) {
-  return key * D + ((chunk ^ (key & 7)) << 3);
+  if constexpr (D == 128) return key * D + ((chunk ^ (key & 15)) << 3);
+  else return key * D + ((chunk ^ ((key >> 1) & 7)) << 3);
 }
-// V^T block in LDS: [D][64 keys], 8-byte granules (4 keys) xor-swizzled by row.
+// V^T block in LDS: [D][64 keys] (128-byte rows), 8-byte granules (4 keys)
+// xor-swizzled by ((d / 2) ^ (d / 8)) % 16: a 32-lane cycle of the PV
+// fragment read (rows d .. d + 31, one granule) and of the transposing stores
+// (rows 8 u + e) then spread over all 64 banks.
 __device__ __forceinline__ int vt_off(int d, int key) {
-  return d * KB + ((((key >> 2) ^ (d & 15)) << 2) | (key & 3));
+  return d * KB + ((((key >> 2) ^ (((d >> 1) ^ (d >> 3)) & 15)) << 2) | (key & 3));
 }
 
 template <int D, int G>
