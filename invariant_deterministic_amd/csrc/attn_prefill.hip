@@ -25,10 +25,13 @@
 // wave's 32 keys:
 //   S^T[key][q] = K Q^T   with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
 //                         B = Q held in registers), D/16 steps ascending;
-//   m_new = max(m, rowmax S), alpha = exp2(m - m_new), P = exp2(S - m_new)
-//   in fp32, l = l * alpha + rowsum(P) (fixed in-lane order plus one lane
-//   exchange), O^T = O^T * alpha + V^T P^T with the same MFMA (A = V^T from a
-//   transposed LDS copy, B = P split into two bf16 terms, see below).
+//   the row's reference maximum m moves to rowmax S only when that exceeds
+//   m by more than 8 (log2 units), so weights stay <= 2^8 and O is rescaled
+//   rarely: alpha = exp2(m - m_new), P = exp2(S - m_new) in fp32,
+//   l = l * alpha + rowsum(P) (fixed in-lane order plus one lane exchange),
+//   O^T = O^T * alpha + V^T P^T with the same MFMA (A = V^T from a transposed
+//   LDS copy, B = P split into two bf16 terms, see below).  Each decision is
+//   the row's own, so it depends on nothing outside the query's keys.
 // Scores are in log2 units (scale * log2(e) applied to S in fp32).  Merge:
 // M = max(m0, m1), a_i = exp2(m_i - M), output bf16((O0 a0 + O1 a1) / (l0 a0
 // + l1 a1)).
@@ -162,9 +165,11 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     const int tile_pos = tile * P;
     const int wpos = tile_pos + QW * pg;               // first position of this wave's queries
     const bool wave_active = wpos <= last_pos && wpos + QW - 1 >= sq.q_start;
-    const int wave_last_blk = wpos / KB;               // diagonal block of the wave
+    // (wave-uniform values, made scalar so the branches below are uniform)
+    const int wave_last_blk = __builtin_amdgcn_readfirstlane(wpos / KB);  // diagonal block of the wave
     // on the diagonal block the wave's key half may lie wholly after its queries
-    const int wave_end_blk = wave_last_blk + (kh * 32 > (wpos % KB) + QW - 1 ? 0 : 1);
+    const int wave_end_blk =
+        __builtin_amdgcn_readfirstlane(wave_last_blk + (kh * 32 > (wpos % KB) + QW - 1 ? 0 : 1));
     const int n_blk = min(tile_pos + P - 1, last_pos) / KB + 1;  // blocks the work-group loads
 
     // queries: B operand of S^T = K Q^T, lane holds Q[pos = wpos + l32][dims (2 kk + hf) * 8 .. + 8]
@@ -219,15 +224,21 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         const int qpos = wpos + l32;
         float mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = blk * KB + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
-          float v = s[r] * sscale;
-          if (diag && (key > qpos || key >= kv_valid)) v = -INFINITY;
-          s[r] = v;
-          mx = fmaxf(mx, v);
+        for (int r = 0; r < 16; ++r) s[r] *= sscale;
+        if (diag) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = blk * KB + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (key > qpos || key >= kv_valid) s[r] = -INFINITY;
+          }
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
+        // the row's reference maximum moves only when the block's maximum
+        // exceeds it by more than 8 (log2 units): weights stay <= 2^8
+        const bool lift = mx > m_run + 8.0f;
+        const float m_new = lift ? mx : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         float rs = 0.f;
@@ -373,6 +384,7 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t q_row_stride, const ui
 }
 
 }  // namespace bi
+
 
 
 
