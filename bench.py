@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--batch", type=int, default=256, help="decode requests in the mixed step")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-reps", type=int, default=10)
+    p.add_argument("--decode-order", default="split", choices=["split", "prefill"],
+                   help="decode attention: fixed 256-key split (default) or the prefill kernel's key order")
     return p.parse_args()
 
 
@@ -105,7 +107,7 @@ def recorded_traffic(roof):
 
 
 # ------------------------------------------------------------ workloads
-def mixed_workload(torch, bi, synth, B):
+def mixed_workload(torch, bi, synth, B, prefill_order=False):
     H, F, hq, hkv, d = 4096, 12288, 32, 8, 128
     w = dict(gamma1=synth.ones_bf16(H), gamma2=synth.ones_bf16(H),
              w_qkv=synth.quantize_int4_g32(504, (hq + 2 * hkv) * d, H),
@@ -114,7 +116,7 @@ def mixed_workload(torch, bi, synth, B):
              w_down=synth.quantize_int4_g32(508, H, F))
     wd = {k: bi.to_dev(v) if not isinstance(v, tuple) else
           (torch.from_numpy(v[0]).cuda(), torch.from_numpy(v[1].view("int16")).cuda()) for k, v in w.items()}
-    cfg = bi.BlockConfig(H, hq, hkv, d, F, 1e-6, 1e6, int4=True)
+    cfg = bi.BlockConfig(H, hq, hkv, d, F, 1e-6, 1e6, int4=True, decode_prefill_order=prefill_order)
     blk = bi.Block(cfg, wd)
     lens = synth.uniform_ints(501, B, 512, 8192)
     cap = 8192 + 1
@@ -143,7 +145,8 @@ def block_flops_bytes(H, F, hq, hkv, d, tokens, weight_bytes, prefill_T, decode_
 
 def run_mixed(args, torch, bi, synth):
     import numpy as np
-    W = mixed_workload(torch, bi, synth, args.batch)
+    po = args.decode_order == "prefill"
+    W = mixed_workload(torch, bi, synth, args.batch, po)
     blk, x, seqs, kp, vp = W["blk"], W["x"], W["seqs"], W["kp"], W["vp"]
     meta, _ = bi.step_meta(seqs, x.device)
     lay = bi.block_workspace(W["cfg"], seqs)
@@ -155,6 +158,14 @@ def run_mixed(args, torch, bi, synth):
 
     ms = time_steps(torch, step, args.steps, args.warmup)
     tokens = args.batch + 2048
+    # the same step with the other decode order (same weights, cache and inputs)
+    other = "split" if po else "prefill"
+    blk2 = bi.Block(bi.BlockConfig(W["H"], W["hq"], W["hkv"], W["d"], W["F"], 1e-6, 1e6, int4=True,
+                                   decode_prefill_order=not po), W["w_dev"])
+    lay2 = bi.block_workspace(blk2.cfg, seqs)
+    ws2 = torch.empty(lay2.total, dtype=torch.uint8, device=x.device)
+    ms_other = time_steps(torch, lambda: blk2.forward(x, seqs, kp, vp, y=y, ws=ws2, meta=meta), args.steps,
+                          args.warmup)
     H, F, hq, hkv, d = W["H"], W["F"], W["hq"], W["hkv"], W["d"]
     wbytes = sum(v[0].nbytes + v[1].nbytes for k, v in W["w_host"].items() if isinstance(v, tuple))
     lin, att_pf, dec_bytes, t_roof = block_flops_bytes(H, F, hq, hkv, d, tokens, wbytes, 2048, W["lens"])
@@ -170,12 +181,18 @@ def run_mixed(args, torch, bi, synth):
     offs = torch.tensor([s["kv_base"] for s in seqs[:-1]], dtype=torch.int64, device=x.device)
     lens = torch.tensor([s["ctx_len"] + 1 for s in seqs[:-1]], dtype=torch.int32, device=x.device)
     max_len = int(max(s["ctx_len"] + 1 for s in seqs[:-1]))
-    dws = torch.empty(bi.attn_decode_workspace(args.batch, max_len, hq, d), dtype=torch.uint8, device=x.device)
     dout = torch.empty_like(q)
-    t_dec = event_time_ms(torch, lambda: bi.attn_decode(q, kp, vp, offs, lens, max_len, hq, hkv, d,
-                                                        1 / math.sqrt(d), ws=dws, out=dout), args.kernel_reps)
+    if po:
+        order = torch.argsort(-lens.long(), stable=True).int()
+        t_dec = event_time_ms(torch, lambda: bi.attn_decode_prefill_order(
+            q, kp, vp, offs, lens, max_len, hq, hkv, d, 1 / math.sqrt(d), order=order, out=dout), args.kernel_reps)
+    else:
+        dws = torch.empty(bi.attn_decode_workspace(args.batch, max_len, hq, d), dtype=torch.uint8, device=x.device)
+        t_dec = event_time_ms(torch, lambda: bi.attn_decode(q, kp, vp, offs, lens, max_len, hq, hkv, d,
+                                                            1 / math.sqrt(d), ws=dws, out=dout), args.kernel_reps)
+    dec_name = "decode attention (prefill key order)" if po else "decode attention (split-256 + combine)"
     if t_dec >= t_gu:
-        roof = {"kernel": "decode attention (split-256 + combine)", "bound": "hbm",
+        roof = {"kernel": dec_name, "bound": "hbm",
                 "achieved": dec_bytes / (t_dec * 1e-3) / 1e9, "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
     else:
         roof = {"kernel": "int4 GEMM gate/up (M=%d, N=%d, K=%d)" % (M, 2 * F, H), "bound": "mfma",
@@ -193,12 +210,14 @@ def run_mixed(args, torch, bi, synth):
         "dtype": "bf16 activations, int4 weights, fp32 accumulation", "data": "synthetic (seeded)",
         "config": {"workload": "int4 block hidden 4096, FFN 12288, 32/8 heads x 128: mixed step of "
                                f"{args.batch} decodes (KV 512..8192) + one 2048-token prefill chunk",
-                   "tokens_per_step": tokens, "decode_batch": args.batch, "prefill_chunk": 2048},
+                   "tokens_per_step": tokens, "decode_batch": args.batch, "prefill_chunk": 2048,
+                   "decode_order": args.decode_order},
         "roofline": roof,
         "block_roofline": {"t_roof_ms": t_roof * 1e3, "frac": t_roof * 1e3 / ms,
                            "linear_gflop": lin / 1e9, "prefill_attn_gflop": att_pf / 1e9,
                            "decode_kv_gb": dec_bytes / 1e9, "weight_mb": wbytes / 1e6},
         "kernels_ms": {"gemm_w4_gate_up": t_gu, "attn_decode": t_dec},
+        "variants": {f"decode_order_{other}": {"ms_per_step": ms_other, "tokens_per_s": tokens / (ms_other * 1e-3)}},
         "build_id": bi.build_id(),
     }
     if not args.no_cpu:
@@ -274,12 +293,17 @@ def run_decode(args, torch, bi, synth):
     q = bi.to_dev(synth.normal_bf16(402, (B, hq * d)))
     od = torch.from_numpy(offs).cuda()
     ld = torch.from_numpy(lens.astype(np.int32)).cuda()
-    ws = torch.empty(bi.attn_decode_workspace(B, 32768, hq, d), dtype=torch.uint8, device="cuda")
     out = torch.empty_like(q)
-    t = event_time_ms(torch, lambda: bi.attn_decode(q, k, v, od, ld, 32768, hq, hkv, d, 1 / math.sqrt(d),
-                                                    ws=ws, out=out), max(args.kernel_reps, 20))
+    if args.decode_order == "prefill":
+        order = torch.from_numpy(np.argsort(-lens, kind="stable").astype(np.int32)).cuda()
+        t = event_time_ms(torch, lambda: bi.attn_decode_prefill_order(
+            q, k, v, od, ld, 32768, hq, hkv, d, 1 / math.sqrt(d), order=order, out=out), max(args.kernel_reps, 20))
+    else:
+        ws = torch.empty(bi.attn_decode_workspace(B, 32768, hq, d), dtype=torch.uint8, device="cuda")
+        t = event_time_ms(torch, lambda: bi.attn_decode(q, k, v, od, ld, 32768, hq, hkv, d, 1 / math.sqrt(d),
+                                                        ws=ws, out=out), max(args.kernel_reps, 20))
     by = float(lens.sum()) * hkv * d * 2 * 2
-    return {"metric": "decode attention GB/s (split 256)", "value": by / t / 1e6, "unit": "GB/s",
+    return {"metric": f"decode attention GB/s ({args.decode_order})", "value": by / t / 1e6, "unit": "GB/s",
             "ms": t, "frac": by / t / 1e6 / (PEAK_HBM / 1e9),
             "config": {"workload": "B=64, L~U{1..32768}, 32/8 heads x 128"}, "build_id": bi.build_id()}
 

@@ -170,6 +170,26 @@ bi_status bi_attn_decode(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* 
                          int B, int64_t max_kv_len, int Hq, int Hkv, int D, float scale,
                          void* ws, size_t ws_bytes, bi_bf16* o, hipStream_t stream);
 
+/* ------------------------------------- decode attention in prefill key order
+ * The same result as bi_attn_decode, computed with exactly the operations
+ * bi_attn_prefill performs for a query at position L_b - 1 (its 64-key blocks
+ * from position 0, two 32-key halves per block with an online softmax each,
+ * the same sums in the same order), so a token decoded alone gets the bits
+ * it gets when prefilled or verified inside a drafted chunk ("Receipts",
+ * opening paragraph: independent of run-ahead drafting; M-0002 "Limitations":
+ * speculative decoding is open work).  No workspace.
+ *   q, k_all, v_all, kv_offset, kv_len, B, max_kv_len, o: as bi_attn_decode
+ *   (a request whose length is outside 1..max_kv_len gets NaN output);
+ *   order: optional device int32 [B], a permutation of 0..B-1 giving the
+ *   order in which requests start (longest first shortens the step); NULL =
+ *   ascending.  It never changes any request's result.
+ *   D in {64, 128}; Hq / Hkv in {1, 2, 4, 8}.                                 */
+bi_status bi_attn_decode_prefill_order(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* v_all,
+                                       const int64_t* kv_offset, const int32_t* kv_len,
+                                       const int32_t* order, int B, int64_t max_kv_len,
+                                       int Hq, int Hkv, int D, float scale, bi_bf16* o,
+                                       hipStream_t stream);
+
 /* ------------------------------------------------------------ decoder block
  * One forward step of a pre-norm decoder block over a batch of sequences:
  *   n1 = RMSNorm(x, gamma1); qkv = n1 Wqkv^T; q, k = RoPE(q, k); append k, v;
@@ -177,8 +197,11 @@ bi_status bi_attn_decode(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* 
  *   [FFN] n2 = RMSNorm(h, gamma2); gu = n2 Wgu^T; act = silu(g) u;
  *         d = act Wdown^T; y = h + d      (without FFN, y = h)
  * with a bf16 rounding at every arrow.  Sequences with q_len == 1 use decode
- * attention; longer ones use prefill attention.                             */
+ * attention (bi_attn_decode, or bi_attn_decode_prefill_order when
+ * decode_order is BI_DECODE_PREFILL_ORDER); longer ones use prefill
+ * attention.                                                                */
 typedef enum { BI_WEIGHTS_BF16 = 0, BI_WEIGHTS_INT4_G32 = 1 } bi_weight_format;
+typedef enum { BI_DECODE_SPLIT = 0, BI_DECODE_PREFILL_ORDER = 1 } bi_decode_order;
 
 typedef struct {
   int hidden;        /* H, % 8 == 0 */
@@ -189,6 +212,8 @@ typedef struct {
   float eps;         /* RMSNorm epsilon */
   double rope_theta; /* 0 = no rotary embedding */
   int weight_format; /* bi_weight_format */
+  int decode_order;  /* bi_decode_order: fixed 256-key split (default), or the
+                        prefill kernel's key order (decoded bits = prefilled) */
 } bi_block_cfg;
 
 typedef struct {

@@ -35,7 +35,8 @@ class BiError(RuntimeError):
 
 class bi_block_cfg(ctypes.Structure):
     _fields_ = [("hidden", c_int), ("n_q_heads", c_int), ("n_kv_heads", c_int), ("head_dim", c_int),
-                ("ffn", c_int), ("eps", c_float), ("rope_theta", c_double), ("weight_format", c_int)]
+                ("ffn", c_int), ("eps", c_float), ("rope_theta", c_double), ("weight_format", c_int),
+                ("decode_order", c_int)]
 
 
 class bi_weight(ctypes.Structure):
@@ -78,6 +79,8 @@ _SIGNATURES = {
     "bi_attn_decode_workspace": (c_size_t, [c_int, c_int64, c_int, c_int]),
     "bi_attn_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int,
                                c_int, c_int, c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "bi_attn_decode_prefill_order": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                             c_int64, c_int, c_int, c_int, c_float, c_void_p, c_void_p]),
     "bi_step_meta_bytes": (c_size_t, [ctypes.POINTER(bi_seq), c_int]),
     "bi_step_pack": (c_int, [ctypes.POINTER(bi_seq), c_int, c_void_p, c_size_t]),
     "bi_block_workspace": (c_int, [ctypes.POINTER(bi_block_cfg), ctypes.POINTER(bi_seq), c_int,
@@ -242,6 +245,20 @@ def attn_decode(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq, Hkv, D, scal
     return out
 
 
+def attn_decode_prefill_order(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq, Hkv, D, scale,
+                              order=None, out=None):
+    _dev(q, BF16, "q"); _dev(k_all, BF16, "k_all"); _dev(v_all, BF16, "v_all")
+    _dev(kv_offset, torch.int64, "kv_offset"); _dev(kv_len, torch.int32, "kv_len")
+    if order is not None:
+        _dev(order, torch.int32, "order")
+    B = q.shape[0]
+    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_attn_decode_prefill_order(_ptr(q), _ptr(k_all), _ptr(v_all), _ptr(kv_offset), _ptr(kv_len),
+                                              _ptr(order), B, int(max_kv_len), Hq, Hkv, D, float(scale),
+                                              _ptr(out), _stream()), "bi_attn_decode_prefill_order")
+    return out
+
+
 # ------------------------------------------------------------------ block
 @dataclass
 class BlockConfig:
@@ -253,11 +270,13 @@ class BlockConfig:
     eps: float = 1e-6
     rope_theta: float = 0.0
     int4: bool = False
+    decode_prefill_order: bool = False  # decode in the prefill kernel's key order
 
     def c(self):
         return bi_block_cfg(self.hidden, self.n_q_heads, self.n_kv_heads, self.head_dim, self.ffn,
                             self.eps, float(self.rope_theta),
-                            BI_WEIGHTS_INT4_G32 if self.int4 else BI_WEIGHTS_BF16)
+                            BI_WEIGHTS_INT4_G32 if self.int4 else BI_WEIGHTS_BF16,
+                            1 if self.decode_prefill_order else 0)
 
 
 def _seq_array(seqs):

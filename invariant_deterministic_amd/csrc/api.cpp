@@ -67,11 +67,12 @@ bool scale_ok(float s) { return s > 0.f && s < 3.0e38f; }
 
 // ---- step metadata layout (host bytes uploaded by the caller)
 struct MetaLayout {
-  size_t prefill, decode, pos, kv, units, total;
+  size_t prefill, decode, pos, kv, units, order, total;
 };
 // Layout of the packed step description: header, prefill descriptors, decode
-// descriptors, per-row positions, per-row KV rows, then the decode unit list
-// (one (request, unit) int32 pair per 256 keys of each decode request).
+// descriptors, per-row positions, per-row KV rows, the decode unit list
+// (one (request, unit) int32 pair per 256 keys of each decode request), then
+// the decode requests ordered longest first (int32 indices).
 MetaLayout meta_layout(int n_seqs, int64_t n_tokens, int64_t n_units) {
   MetaLayout L;
   L.prefill = 256;
@@ -79,7 +80,8 @@ MetaLayout meta_layout(int n_seqs, int64_t n_tokens, int64_t n_units) {
   L.pos = L.decode + align256(size_t(n_seqs) * sizeof(DecodeSeq));
   L.kv = L.pos + align256(size_t(n_tokens) * sizeof(int32_t));
   L.units = L.kv + align256(size_t(n_tokens) * sizeof(int64_t));
-  L.total = L.units + align256(size_t(n_units) * 8);
+  L.order = L.units + align256(size_t(n_units) * 8);
+  L.total = L.order + align256(size_t(n_seqs) * sizeof(int32_t));
   return L;
 }
 int64_t decode_units(const bi_seq* seqs, int n_seqs) {
@@ -129,6 +131,8 @@ bi_status check_cfg(const bi_block_cfg* c) {
   if (!(c->rope_theta >= 0.0) || c->rope_theta > 1e300) return BI_ERR_SHAPE;
   if (c->weight_format != BI_WEIGHTS_BF16 && c->weight_format != BI_WEIGHTS_INT4_G32)
     return BI_ERR_UNSUPPORTED;
+  if (c->decode_order != BI_DECODE_SPLIT && c->decode_order != BI_DECODE_PREFILL_ORDER)
+    return BI_ERR_UNSUPPORTED;
   return BI_OK;
 }
 
@@ -171,9 +175,9 @@ WsLayout ws_layout(const bi_block_cfg& c, const StepSummary& s) {
   L.pub.act = F ? take(M * F * 2) : none;
   L.pub.d = F ? take(M * H * 2) : none;
   L.pub.decode_partials =
-      s.n_decode ? take(bi::decode_workspace_bytes(s.n_decode, s.max_decode_len, c.n_q_heads,
-                                                   c.head_dim))
-                 : none;
+      s.n_decode && c.decode_order == BI_DECODE_SPLIT
+          ? take(bi::decode_workspace_bytes(s.n_decode, s.max_decode_len, c.n_q_heads, c.head_dim))
+          : none;
   L.pub.total = off;
   return L;
 }
@@ -324,6 +328,24 @@ bi_status bi_attn_decode(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* 
                                                 Hq, Hkv, D, scale, ws, o, stream));
 }
 
+bi_status bi_attn_decode_prefill_order(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* v_all,
+                                       const int64_t* kv_offset, const int32_t* kv_len,
+                                       const int32_t* order, int B, int64_t max_kv_len, int Hq,
+                                       int Hkv, int D, float scale, bi_bf16* o, hipStream_t stream) {
+  if (!q || !k_all || !v_all || !kv_offset || !kv_len || !o) return BI_ERR_NULL;
+  if (B < 1 || max_kv_len < 1) return BI_ERR_SHAPE;
+  if (B > 65535 || max_kv_len > (int64_t(1) << 30)) return BI_ERR_UNSUPPORTED;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
+  if (!head_shape_ok(Hq, Hkv, D, 8)) return BI_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return BI_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_all) || !aligned16(v_all) || !aligned16(o) || !aligned8(kv_offset) ||
+      (reinterpret_cast<uintptr_t>(kv_len) & 3u) || (reinterpret_cast<uintptr_t>(order) & 3u))
+    return BI_ERR_ALIGN;
+  return from_hip(bi::launch_attn_decode_po(q, int64_t(Hq) * D, k_all, v_all, nullptr, kv_offset, kv_len,
+                                            order, B, max_kv_len, Hq, Hkv, D, scale, o, int64_t(Hq) * D,
+                                            stream));
+}
+
 size_t bi_step_meta_bytes(const bi_seq* seqs, int n_seqs) {
   StepSummary s;
   if (summarize(seqs, n_seqs, &s) != BI_OK) return 0;
@@ -382,6 +404,10 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
     }
     row += q.q_len;
   }
+  // decode requests longest first (ties by index): only the launch order
+  int32_t* order = at<int32_t>(host_meta, L.order);
+  for (int i = 0; i < nd; ++i) order[i] = i;
+  std::stable_sort(order, order + nd, [&](int32_t a, int32_t b) { return dc[a].kv_len > dc[b].kv_len; });
   return BI_OK;
 }
 
@@ -465,7 +491,11 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
                                    at<PrefillSeq>(d_meta, ML.prefill), nullptr, s.n_prefill,
                                    max_tiles, Hq, Hkv, D, scale, stream));
   }
-  if (s.n_decode) {
+  if (s.n_decode && c.decode_order == BI_DECODE_PREFILL_ORDER) {
+    BI_TRY(bi::launch_attn_decode_po(q, int64_t(Hq) * D, kv->k, kv->v, at<DecodeSeq>(d_meta, ML.decode),
+                                     nullptr, nullptr, at<int32_t>(d_meta, ML.order), s.n_decode,
+                                     s.max_decode_len, Hq, Hkv, D, scale, attn, int64_t(Hq) * D, stream));
+  } else if (s.n_decode) {
     BI_TRY(bi::launch_attn_decode(q, int64_t(Hq) * D, kv->k, kv->v, at<DecodeSeq>(d_meta, ML.decode),
                                   at<int2>(d_meta, ML.units), int(n_units), s.n_decode,
                                   s.max_decode_len, Hq, Hkv, D, scale,

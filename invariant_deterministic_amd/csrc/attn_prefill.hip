@@ -22,19 +22,28 @@
 //    are always masked.
 //
 // Per wave and block (D = head_dim, G = query heads per kv head), for the
-// wave's 32 keys:
-//   S^T[key][q] = K Q^T   with v_mfma_f32_32x32x16_bf16 (A = K from LDS,
+// wave's 32 keys.  Within a half, key 4 j + c (j = 0..7) is "class" c = 0..3;
+// every sum below groups the keys by class, in a layout a one-query decode
+// kernel can reproduce operation for operation (so a token's bits do not
+// depend on whether it was prefilled or decoded):
+//   S^T[key][q] = K Q^T   with v_mfma_f32_32x32x16_bf16 (A = K from LDS, its
+//                         rows permuted so that output register r of lane
+//                         half hf holds class 2 (r / 8) + hf, j = r % 8;
 //                         B = Q held in registers), D/16 steps ascending;
 //   the row's reference maximum m moves to rowmax S only when that exceeds
 //   m by more than 8 (log2 units), so weights stay <= 2^8 and O is rescaled
 //   rarely: alpha = exp2(m - m_new), P = exp2(S - m_new) in fp32,
-//   l = l * alpha + rowsum(P) (fixed in-lane order plus one lane exchange),
+//   rowsum(P) = ((sum c0 + sum c2) + (sum c1 + sum c3)), each class summed in
+//   ascending j, l = fma(l, alpha, rowsum);
 //   O^T = O^T * alpha + V^T P^T with the same MFMA (A = V^T from a transposed
-//   LDS copy, B = P split into two bf16 terms, see below).  Each decision is
-//   the row's own, so it depends on nothing outside the query's keys.
+//   LDS copy whose keys are stored class by class, B = P split into two bf16
+//   terms, see below), four instructions per 32 dims: P_hi of classes 0 and
+//   1, P_hi of 2 and 3, P_lo of 0 and 1, P_lo of 2 and 3 (each instruction
+//   adds two 8-key groups in order).  Each decision is the row's own, so it
+//   depends on nothing outside the query's keys.
 // Scores are in log2 units (scale * log2(e) applied to S in fp32).  Merge:
-// M = max(m0, m1), a_i = exp2(m_i - M), output bf16((O0 a0 + O1 a1) / (l0 a0
-// + l1 a1)).
+// M = max(m0, m1), a_i = exp2(m_i - M), output
+// bf16(fma(O0, a0, O1 a1) / fma(l0, a0, l1 a1)).
 //
 // Work-group = 8 waves = (kv head g, tile of P = 128 / G positions): wave w
 // takes query head g*G + w % G, key half (w / G) % 2 and the 32 positions
@@ -65,12 +74,24 @@ __device__ __forceinline__ int k_off(int key, int chunk) {
   if constexpr (D == 128) return key * D + ((chunk ^ (key & 15)) << 3);
   else return key * D + ((chunk ^ ((key >> 1) & 7)) << 3);
 }
-// V^T block in LDS: [D][64 keys] (128-byte rows), 8-byte granules (4 keys)
-// xor-swizzled by ((d / 2) ^ (d / 8)) % 16: a 32-lane cycle of the PV
-// fragment read (rows d .. d + 31, one granule) and of the transposing stores
-// (rows 8 u + e) then spread over all 64 banks.
-__device__ __forceinline__ int vt_off(int d, int key) {
-  return d * KB + ((((key >> 2) ^ (((d >> 1) ^ (d >> 3)) & 15)) << 2) | (key & 3));
+// K block row of key k (0..63): within each 32-key half, MFMA row i holds key
+// 4 j + c with c = 2 (i / 16) + (i / 4) % 2 and j = 4 ((i / 8) % 2) + i % 4,
+// which puts class c = 2 (r / 8) + hf, j = r % 8 into output register r of
+// lane half hf.
+__device__ __forceinline__ int k_row(int k) {
+  const int c = k & 3, j = (k >> 2) & 7;
+  return (k & 32) | ((c >> 1) << 4) | ((j >> 2) << 3) | ((c & 1) << 2) | (j & 3);
+}
+// V^T block in LDS: [D][64 positions], position 32 h + 8 c + j holding key
+// 32 h + 4 j + c (the keys of a half stored class by class), in 8-byte
+// granules (4 positions) xor-swizzled by ((d / 2) ^ (d / 8)) % 16: a 32-lane
+// cycle of the PV fragment read (rows d .. d + 31, one granule) and of the
+// transposing stores (rows 8 u + e) then spread over all 64 banks.
+__device__ __forceinline__ int vt_off(int d, int pos) {
+  return d * KB + ((((pos >> 2) ^ (((d >> 1) ^ (d >> 3)) & 15)) << 2) | (pos & 3));
+}
+__device__ __forceinline__ int key_at_pos(int pos) {
+  return (pos & 32) | ((pos & 7) << 2) | ((pos >> 3) & 3);
 }
 
 template <int D, int G>
@@ -128,7 +149,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
                                                wave_uniform(uint32_t(nvalid) * uint32_t(kv_stride) * 2));
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int key = is_k ? ur + (HT / DCH) * i : KPT * ur + i;
+      const int key = is_k ? ur + (HT / DCH) * i : key_at_pos(KPT * ur + i);
       const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
           rs, int(uint32_t(key) * uint32_t(kv_stride) * 2 + uint32_t(uc) * 16), 0, 0);
       rr[i] = make_uint4(v.x, v.y, v.z, v.w);
@@ -138,7 +159,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     if (is_k) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i)
-        *reinterpret_cast<uint4*>(&sKV[0][stage][k_off<D>(ur + (HT / DCH) * i, uc)]) = rr[i];
+        *reinterpret_cast<uint4*>(&sKV[0][stage][k_off<D>(k_row(ur + (HT / DCH) * i), uc)]) = rr[i];
     } else {
       const uint32_t* w32 = reinterpret_cast<const uint32_t*>(rr);
 #pragma unroll
@@ -219,7 +240,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cK + k_off<D>(32 * kh + l32, 2 * kk + hf));
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
         }
-        // lane holds query wpos + l32 and keys blk*64 + 32 kh + 8 (r / 4) + 4 hf + r % 4
+        // lane holds query wpos + l32; register r the key of class 2 (r / 8) + hf, j = r % 8
         const bool diag = blk == wave_last_blk;
         const int qpos = wpos + l32;
         float mx = -INFINITY;
@@ -228,7 +249,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         if (diag) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = blk * KB + 32 * kh + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const int key = blk * KB + 32 * kh + 4 * (r & 7) + 2 * (r >> 3) + hf;
             if (key > qpos || key >= kv_valid) s[r] = -INFINITY;
           }
         }
@@ -241,15 +262,18 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         const float m_new = lift ? mx : m_run;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
-        float rs = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = __builtin_amdgcn_exp2f(s[r] - m_new);
-          s[r] = pv;
-          rs += pv;
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
+        // per class in ascending j, then (c0 + c2) + (c1 + c3)
+        float sa = s[0], sb = s[8];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) {
+          sa += s[j];
+          sb += s[8 + j];
         }
-        rs += __shfl_xor(rs, 32, 64);
-        l_run = l_run * alpha + rs;
+        const float tc = sa + sb;
+        const float rs = tc + __shfl_xor(tc, 32, 64);
+        l_run = __builtin_fmaf(l_run, alpha, rs);
         if (__any(alpha != 1.0f)) {
 #pragma unroll
           for (int bd = 0; bd < BD; ++bd)
@@ -258,12 +282,13 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         }
         // the next block goes into the free stage here, overlapping the PV MFMAs
         if (blk + 1 < n_blk) store_block(cur ^ 1);
-        // O^T[d][q] += V^T[d][key] P^T[key][q], P = hi + lo in bf16; MFMA
-        // k-slot hf*8 + e of step `half` is key 32 kh + 16 half + 8 (e / 4) +
-        // 4 hf + e % 4 = register 8 half + e of S^T.
+        // O^T[d][q] += V^T[d][key] P^T[key][q], P = hi + lo in bf16.  MFMA
+        // k-slot e of lane half hf in instruction `half` is register
+        // 8 half + e of S^T: key 4 e + c of class c = 2 half + hf, V^T
+        // positions 32 kh + 8 c + e.  Order: hi(0), hi(1), lo(0), lo(1).
+        bf16x8 p_hi[2], p_lo[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int key_a = 32 * kh + 16 * half + 4 * hf;
           uint32_t hw[4], lw[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -273,17 +298,24 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
             hw[e] = hp;
             lw[e] = pack2bf(a - bf2f_lo(hp), b - bf2f_hi(hp));
           }
-          const bf16x8 p_hi = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
-          const bf16x8 p_lo = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+          p_hi[half] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
+          p_lo[half] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
+        }
 #pragma unroll
-          for (int bd = 0; bd < BD; ++bd) {
-            const int d = 32 * bd + l32;
-            const uint2 lo = *reinterpret_cast<const uint2*>(cV + vt_off(d, key_a));
-            const uint2 hi = *reinterpret_cast<const uint2*>(cV + vt_off(d, key_a + 8));
-            const bf16x8 vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-            acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_hi, acc_o[bd], 0, 0, 0);
-            acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_lo, acc_o[bd], 0, 0, 0);
+        for (int bd = 0; bd < BD; ++bd) {
+          const int d = 32 * bd + l32;
+          bf16x8 vf[2];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int pos = 32 * kh + 8 * (2 * half + hf);
+            const uint2 lo = *reinterpret_cast<const uint2*>(cV + vt_off(d, pos));
+            const uint2 hi = *reinterpret_cast<const uint2*>(cV + vt_off(d, pos + 4));
+            vf[half] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
           }
+          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0], p_hi[0], acc_o[bd], 0, 0, 0);
+          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], p_hi[1], acc_o[bd], 0, 0, 0);
+          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0], p_lo[0], acc_o[bd], 0, 0, 0);
+          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], p_lo[1], acc_o[bd], 0, 0, 0);
         }
       }
       if (!(wave_active && blk < wave_end_blk) && blk + 1 < n_blk) store_block(cur ^ 1);  // idle waves
@@ -313,7 +345,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         const float mm = fmaxf(m_run, m1);
         const float a0 = __builtin_amdgcn_exp2f(m_run - mm);
         const float a1 = __builtin_amdgcn_exp2f(m1 - mm);
-        const float inv = 1.0f / (l_run * a0 + l1 * a1);
+        const float inv = 1.0f / __builtin_fmaf(l_run, a0, l1 * a1);
         uint16_t* dst = o + (sq.q_row + (pos - sq.q_start)) * o_stride + h * D;
 #pragma unroll
         for (int bd = 0; bd < BD; ++bd)
@@ -323,7 +355,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const int r = 4 * rg + j;
-              ov[j] = (acc_o[bd][r] * a0 + sm[((slot * BD + bd) * 16 + r) * 64 + lane] * a1) * inv;
+              ov[j] = __builtin_fmaf(acc_o[bd][r], a0, sm[((slot * BD + bd) * 16 + r) * 64 + lane] * a1) * inv;
             }
             const int d = 32 * bd + 8 * rg + 4 * hf;
             uint2 v;

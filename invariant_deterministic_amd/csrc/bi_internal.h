@@ -74,4 +74,14 @@ hipError_t launch_attn_decode_arrays(const uint16_t* q, const uint16_t* k_all,
                                      int Hkv, int D, float scale, void* ws, uint16_t* o,
                                      hipStream_t s);
 
+// Decode attention in the prefill kernel's key order (bitwise equal to prefill
+// for the same query).  Request descriptors come from d_seqs, or, when d_seqs
+// is nullptr, from the offset / length arrays with q_row = b.  d_order
+// (optional) is a permutation of 0..B-1: the launch order of the requests.
+hipError_t launch_attn_decode_po(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_all,
+                                 const uint16_t* v_all, const DecodeSeq* d_seqs, const int64_t* kv_offset,
+                                 const int32_t* kv_len, const int32_t* d_order, int B, int64_t max_kv_len,
+                                 int Hq, int Hkv, int D, float scale, uint16_t* o, int64_t o_row_stride,
+                                 hipStream_t s);
+
 }  // namespace bi
