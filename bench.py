@@ -37,7 +37,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--config", default="mixed", choices=["mixed", "dense", "gemm", "decode", "norm", "tiny", "copy"])
+    p.add_argument("--config", default="mixed",
+                   choices=["mixed", "dense", "gemm", "decode", "norm", "tiny", "copy", "lmhead"])
     p.add_argument("--batch", type=int, default=256, help="decode requests in the mixed step")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-reps", type=int, default=10)
@@ -376,6 +377,54 @@ def run_tiny(args, torch, bi, synth):
             "build_id": bi.build_id()}
 
 
+def run_lmhead(args, torch, bi, synth):
+    """The step after the block for 256 decode rows: final RMSNorm, LM head (hidden 4096,
+    vocabulary 151936), seeded sampling with the receipt page's settings, token hashes."""
+    import numpy as np
+    B, H, V, NH = 256, 4096, 151936, 64
+    x = synth.normal_bf16_device(1300, (B, H))
+    g = bi.to_dev(synth.normal_bf16(1301, (H,), 0.02, 1.0))
+    w = synth.normal_bf16_device(1302, (V, H), 0.02)
+    rng = np.random.default_rng(1303)
+    hist = torch.from_numpy(rng.integers(0, V, size=(B, NH)).astype(np.int32)).cuda()
+    seeds = torch.from_numpy(rng.integers(0, 2 ** 62, size=B).astype(np.int64)).cuda()
+    pos = torch.from_numpy(rng.integers(512, 8192, size=B).astype(np.int64)).cuda()
+    n = torch.empty_like(x)
+    logits = torch.empty((B, V), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty(B, dtype=torch.int32, device="cuda")
+    seq = torch.empty((B, NH + 1), dtype=torch.int32, device="cuda")
+    seq[:, :NH] = hist
+    offs = torch.arange(B, dtype=torch.int64, device="cuda") * (NH + 1)
+    cnts = torch.full((B,), NH + 1, dtype=torch.int32, device="cuda")
+    digests = torch.empty((B, 32), dtype=torch.uint8, device="cuda")
+    prm = dict(temperature=0.8, top_k=50, top_p=0.95, min_p=0.05, repeat=1.1)
+
+    def sample():
+        bi.sample(logits, seeds, pos, history=hist, out=ids, **prm)
+
+    def step():
+        bi.rmsnorm(x, g, 1e-6, out=n)
+        bi.gemm(n, w, out=logits)
+        sample()
+        seq[:, NH] = ids
+        bi.token_hash(seq, offs, cnts, out=digests)
+
+    ms = time_steps(torch, step, args.steps, args.warmup)
+    t_gemm = event_time_ms(torch, lambda: bi.gemm(n, w, out=logits), max(args.kernel_reps, 10))
+    t_samp = event_time_ms(torch, sample, max(args.kernel_reps, 10))
+    t_hash = event_time_ms(torch, lambda: bi.token_hash(seq, offs, cnts, out=digests), max(args.kernel_reps, 10))
+    fl = 2.0 * B * V * H
+    wb = 2.0 * V * H
+    return {"metric": "step after the block tokens/s", "value": B / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "config": {"workload": f"final RMSNorm + LM head (hidden {H}, vocabulary {V}) + seeded sampling "
+                                   f"(T 0.8, top-k 50, top-p 0.95, min-p 0.05, repeat 1.1 over {NH}) + token hashes, "
+                                   f"{B} rows"},
+            "kernels_ms": {"lm_head_gemm": t_gemm, "sample": t_samp, "token_hash": t_hash},
+            "lm_head": {"tflops": fl / t_gemm / 1e9, "frac_mfma": fl / t_gemm / 1e9 / (PEAK_BF16 / 1e12),
+                        "weight_gbs": wb / t_gemm / 1e6, "frac_hbm": wb / t_gemm / 1e6 / (PEAK_HBM / 1e9)},
+            "build_id": bi.build_id()}
+
+
 def run_copy(args, torch, bi, synth):
     """A plain 1 GiB device copy (torch), the reference for scaling HBM counters."""
     n = 1 << 29
@@ -399,7 +448,7 @@ def main():
         sys.exit(1)
     bi.lib()
     fn = {"mixed": run_mixed, "dense": run_dense, "gemm": run_gemm, "decode": run_decode,
-          "norm": run_norm, "tiny": run_tiny, "copy": run_copy}[args.config]
+          "norm": run_norm, "tiny": run_tiny, "copy": run_copy, "lmhead": run_lmhead}[args.config]
     out = fn(args, torch, bi, synth)
     print(json.dumps(out), flush=True)
 

@@ -190,6 +190,51 @@ bi_status bi_attn_decode_prefill_order(const bi_bf16* q, const bi_bf16* k_all, c
                                        int Hq, int Hkv, int D, float scale, bi_bf16* o,
                                        hipStream_t stream);
 
+/* ------------------------------------------------- the step after the block
+ * Seeded sampling of the next token for each row of logits (after the final
+ * RMSNorm, bi_rmsnorm, and the LM head, bi_gemm with N = vocabulary), and
+ * BLAKE3 hashes of token ids as a receipt records them ("Receipts", "Making a
+ * receipt": prompt and output ids with their BLAKE3 over little-endian
+ * 32-bit integers; the sampler settings and the seed).  A row's token depends
+ * only on its logits, history, seed and position, never on the batch.
+ * Sampler, per row:
+ *   1. penalties (fp32) for each distinct history token: repeat
+ *      (l > 0 ? l / r : l * r), then l - (presence + count * frequency);
+ *   2. temperature 0: the largest logit, lowest id on ties;
+ *   3. otherwise the top_k logits ordered by (logit desc, id asc); in fp64
+ *      w = exp((l - l_max) / T); min-p keeps w >= min_p; top-p keeps the
+ *      shortest prefix whose running sum reaches top_p of the total; the
+ *      token is the first whose running sum exceeds u times the kept total,
+ *      u = (first word of Philox4x64-10, key (seed, 0), counter
+ *      (position, 0, 0, 0)) >> 11, times 2^-53.                              */
+typedef struct {
+  float temperature;       /* >= 0; 0 = greedy */
+  int   top_k;             /* 1..1024 when temperature > 0 */
+  float top_p;             /* (0, 1] */
+  float min_p;             /* [0, 1) */
+  float repeat_penalty;    /* > 0; 1 = off */
+  float presence_penalty;  /* 0 = off */
+  float frequency_penalty; /* 0 = off */
+} bi_sampling;
+
+/*   logits [rows, vocab] bf16, 16-byte aligned, vocab % 8 == 0, vocab <= 2^24
+ *   (the LM head GEMM needs N % 8 == 0 as well);
+ *   params: host; seeds [rows] uint64 and positions [rows] int64 (device);
+ *   history [rows, n_hist] int32 device, 0 <= n_hist <= 256 (ids outside
+ *   0..vocab-1 are ignored; may be NULL when n_hist == 0);
+ *   out_ids [rows] int32 device.                                             */
+bi_status bi_sample(const bi_bf16* logits, int64_t rows, int64_t vocab, const bi_sampling* params,
+                    const uint64_t* seeds, const int64_t* positions, const int32_t* history,
+                    int n_hist, int32_t* out_ids, hipStream_t stream);
+
+/* BLAKE3 (hash mode, 32 bytes) of each sequence's ids as little-endian
+ * 32-bit integers.  ids: device int32; offsets [n_seqs] int64 and counts
+ * [n_seqs] int32 (device): sequence s is ids[offsets[s] .. + counts[s]).
+ * out [n_seqs, 32] bytes (device).  A count outside 0..65536 (which the host
+ * cannot see) gives an all-ones digest for that sequence.                    */
+bi_status bi_token_hash(const int32_t* ids, const int64_t* offsets, const int32_t* counts, int n_seqs,
+                        uint8_t* out, hipStream_t stream);
+
 /* ------------------------------------------------------------ decoder block
  * One forward step of a pre-norm decoder block over a batch of sequences:
  *   n1 = RMSNorm(x, gamma1); qkv = n1 Wqkv^T; q, k = RoPE(q, k); append k, v;

@@ -56,6 +56,11 @@ class bi_kv_pool(ctypes.Structure):
     _fields_ = [("k", c_void_p), ("v", c_void_p), ("rows", c_int64)]
 
 
+class bi_sampling(ctypes.Structure):
+    _fields_ = [("temperature", c_float), ("top_k", c_int), ("top_p", c_float), ("min_p", c_float),
+                ("repeat_penalty", c_float), ("presence_penalty", c_float), ("frequency_penalty", c_float)]
+
+
 class bi_block_ws_layout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("n1", "qkv", "q", "attn", "o", "h", "n2", "gu", "act", "d",
                                         "decode_partials", "total")]
@@ -81,6 +86,9 @@ _SIGNATURES = {
                                c_int, c_int, c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
     "bi_attn_decode_prefill_order": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                                              c_int64, c_int, c_int, c_int, c_float, c_void_p, c_void_p]),
+    "bi_sample": (c_int, [c_void_p, c_int64, c_int64, ctypes.POINTER(bi_sampling), c_void_p, c_void_p, c_void_p,
+                          c_int, c_void_p, c_void_p]),
+    "bi_token_hash": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
     "bi_step_meta_bytes": (c_size_t, [ctypes.POINTER(bi_seq), c_int]),
     "bi_step_pack": (c_int, [ctypes.POINTER(bi_seq), c_int, c_void_p, c_size_t]),
     "bi_block_workspace": (c_int, [ctypes.POINTER(bi_block_cfg), ctypes.POINTER(bi_seq), c_int,
@@ -256,6 +264,31 @@ def attn_decode_prefill_order(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq
     _check(lib().bi_attn_decode_prefill_order(_ptr(q), _ptr(k_all), _ptr(v_all), _ptr(kv_offset), _ptr(kv_len),
                                               _ptr(order), B, int(max_kv_len), Hq, Hkv, D, float(scale),
                                               _ptr(out), _stream()), "bi_attn_decode_prefill_order")
+    return out
+
+
+def sample(logits, seeds, positions, temperature=0.0, top_k=1, top_p=1.0, min_p=0.0, repeat=1.0,
+           presence=0.0, frequency=0.0, history=None, out=None):
+    """Next token per row of bf16 logits [rows, vocab]; seeds uint64-as-int64 and positions int64 [rows]."""
+    _dev(logits, BF16, "logits"); _dev(seeds, torch.int64, "seeds"); _dev(positions, torch.int64, "positions")
+    rows, vocab = logits.shape
+    n_hist = 0
+    if history is not None:
+        _dev(history, torch.int32, "history")
+        n_hist = history.shape[1]
+    out = torch.empty(rows, dtype=torch.int32, device=logits.device) if out is None else out
+    prm = bi_sampling(temperature, top_k, top_p, min_p, repeat, presence, frequency)
+    _check(lib().bi_sample(_ptr(logits), rows, vocab, ctypes.byref(prm), _ptr(seeds), _ptr(positions), _ptr(history),
+                           n_hist, _ptr(out), _stream()), "bi_sample")
+    return out
+
+
+def token_hash(ids, offsets, counts, out=None):
+    """BLAKE3 of each sequence's int32 ids (device); returns uint8 [n_seqs, 32]."""
+    _dev(ids, torch.int32, "ids"); _dev(offsets, torch.int64, "offsets"); _dev(counts, torch.int32, "counts")
+    n = counts.shape[0]
+    out = torch.empty((n, 32), dtype=torch.uint8, device=ids.device) if out is None else out
+    _check(lib().bi_token_hash(_ptr(ids), _ptr(offsets), _ptr(counts), n, _ptr(out), _stream()), "bi_token_hash")
     return out
 
 

@@ -346,6 +346,48 @@ bi_status bi_attn_decode_prefill_order(const bi_bf16* q, const bi_bf16* k_all, c
                                             stream));
 }
 
+bi_status bi_sample(const bi_bf16* logits, int64_t rows, int64_t vocab, const bi_sampling* params,
+                    const uint64_t* seeds, const int64_t* positions, const int32_t* history, int n_hist,
+                    int32_t* out_ids, hipStream_t stream) {
+  if (!logits || !params || !seeds || !positions || !out_ids) return BI_ERR_NULL;
+  if (n_hist > 0 && !history) return BI_ERR_NULL;
+  if (rows < 1 || vocab < 1 || n_hist < 0) return BI_ERR_SHAPE;
+  if (rows > INT32_MAX || vocab > (int64_t(1) << 24) || vocab % 8 || n_hist > 256) return BI_ERR_UNSUPPORTED;
+  const bi_sampling& p = *params;
+  auto finite = [](float x) { return x == x && x < 3.0e38f && x > -3.0e38f; };
+  if (!finite(p.temperature) || p.temperature < 0.f) return BI_ERR_SHAPE;
+  if (p.temperature > 0.f) {
+    if (p.top_k < 1) return BI_ERR_SHAPE;
+    if (p.top_k > 1024) return BI_ERR_UNSUPPORTED;
+    if (!(p.top_p > 0.f && p.top_p <= 1.f) || !(p.min_p >= 0.f && p.min_p < 1.f)) return BI_ERR_SHAPE;
+  }
+  if (!finite(p.repeat_penalty) || !(p.repeat_penalty > 0.f) || !finite(p.presence_penalty) ||
+      !finite(p.frequency_penalty))
+    return BI_ERR_SHAPE;
+  if (!aligned16(logits) || !aligned8(seeds) || !aligned8(positions) ||
+      (reinterpret_cast<uintptr_t>(history) & 3u) || (reinterpret_cast<uintptr_t>(out_ids) & 3u))
+    return BI_ERR_ALIGN;
+  bi::BiSampling q;
+  q.temperature = p.temperature;
+  q.top_k = p.top_k;
+  q.top_p = p.top_p;
+  q.min_p = p.min_p;
+  q.repeat = p.repeat_penalty;
+  q.presence = p.presence_penalty;
+  q.frequency = p.frequency_penalty;
+  return from_hip(bi::launch_sample(logits, rows, vocab, q, seeds, positions, history, n_hist, out_ids, stream));
+}
+
+bi_status bi_token_hash(const int32_t* ids, const int64_t* offsets, const int32_t* counts, int n_seqs,
+                        uint8_t* out, hipStream_t stream) {
+  if (!ids || !offsets || !counts || !out) return BI_ERR_NULL;
+  if (n_seqs < 1) return BI_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(ids) & 3u) || !aligned8(offsets) || (reinterpret_cast<uintptr_t>(counts) & 3u) ||
+      (reinterpret_cast<uintptr_t>(out) & 3u))
+    return BI_ERR_ALIGN;
+  return from_hip(bi::launch_token_hash(ids, offsets, counts, n_seqs, out, stream));
+}
+
 size_t bi_step_meta_bytes(const bi_seq* seqs, int n_seqs) {
   StepSummary s;
   if (summarize(seqs, n_seqs, &s) != BI_OK) return 0;

@@ -84,4 +84,17 @@ hipError_t launch_attn_decode_po(const uint16_t* q, int64_t q_row_stride, const 
                                  int Hq, int Hkv, int D, float scale, uint16_t* o, int64_t o_row_stride,
                                  hipStream_t s);
 
+// Sampler settings (mirrors bi_sampling of the public header).
+struct BiSampling {
+  float temperature;
+  int top_k;
+  float top_p, min_p, repeat, presence, frequency;
+};
+hipError_t launch_sample(const uint16_t* logits, int64_t rows, int64_t vocab, const BiSampling& prm,
+                         const uint64_t* seeds, const int64_t* positions, const int32_t* history, int n_hist,
+                         int32_t* out, hipStream_t s);
+hipError_t launch_token_hash(const int32_t* ids, const int64_t* offsets, const int32_t* counts, int n_seqs,
+                             uint8_t* out, hipStream_t s);
+int token_hash_max_ids();
+
 }  // namespace bi

@@ -24,7 +24,8 @@ nothing but (s, p), so a row's draw does not depend on the batch.
 Sampler.  The pages list the receipt's sampler settings (temperature, top-k,
 top-p, min-p, repeat / presence / frequency penalties over the last n tokens,
 seed) but not the algorithm; this is the plain reading, in this order:
- 1. penalties, in float32, for each distinct token of the row's history:
+ 1. penalties, in float32, for each distinct token of the row's history
+    (ids outside the vocabulary are ignored):
     repeat: l > 0 -> l / r, else l * r; then
     presence and frequency: l - (presence + count * frequency);
  2. temperature 0: the largest penalised logit, lowest id on ties (greedy);
@@ -167,7 +168,7 @@ def uniform(seed: int, position: int) -> float:
 def penalised_logits(logit_bits, history, repeat=1.0, presence=0.0, frequency=0.0) -> np.ndarray:
     """Float32 logits of one row after the history penalties (step 1 of the header)."""
     l = bf16_decode(logit_bits).astype(np.float32)
-    hist = [int(t) for t in history if int(t) >= 0]
+    hist = [int(t) for t in history if 0 <= int(t) < l.size]   # other ids are ignored
     r, pr, fr = np.float32(repeat), np.float32(presence), np.float32(frequency)
     for tok in sorted(set(hist)):
         v = l[tok]
