@@ -45,10 +45,11 @@ namespace {
 constexpr int KB = kPrefillKeyBlock;  // 64 keys per block
 constexpr int NT = 128;               // two waves
 
-template <int D, int G>
+template <int D, int G, bool Q8>
 __global__ __launch_bounds__(NT) void decode_po_kernel(
-    const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_all,
-    const uint16_t* __restrict__ v_all, const DecodeSeq* __restrict__ seqs,
+    const uint16_t* __restrict__ q, int64_t q_stride, const void* __restrict__ k_all,
+    const void* __restrict__ v_all, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    const int32_t* __restrict__ block_tables, int max_pages, const DecodeSeq* __restrict__ seqs,
     const int64_t* __restrict__ kv_offset, const int32_t* __restrict__ kv_len,
     const int32_t* __restrict__ order, int Hkv, int64_t max_len, float sscale,
     uint16_t* __restrict__ o, int64_t o_stride) {
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
     L = sq.kv_len;
   } else {
     qrow = b;
-    koff = kv_offset[b];
+    koff = Q8 ? 0 : kv_offset[b];  // the int8 cache is addressed through block tables
     L = kv_len[b];
   }
   const int lane = threadIdx.x & 63;
@@ -90,8 +91,8 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
 
   const int64_t row_stride = int64_t(Hkv) * D;
   const uint32_t row_bytes = uint32_t(row_stride) * 2;
-  const uint16_t* kbase = k_all + koff * row_stride + g * D;
-  const uint16_t* vbase = v_all + koff * row_stride + g * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(k_all) + koff * row_stride + g * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(v_all) + koff * row_stride + g * D;
   const uint32_t lane_off = uint32_t(grp) * row_bytes + uint32_t(l16) * LD * 2;
 
   // ---- query: the G heads of kv head g, through LDS
@@ -114,6 +115,58 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
     for (int it = 0; it < 8; ++it) buf_ld_stream<NDW>(krs, lane_off + uint32_t(4 * it) * row_bytes, kd[it]);
 #pragma unroll
     for (int it = 0; it < 8; ++it) buf_ld_stream<NDW>(vrs, lane_off + uint32_t(4 * it) * row_bytes, vd[it]);
+  };
+  // int8 paged cache: LD codes per key (NQ dwords) and the key's scale; block blk is page
+  // block_tables[b][blk], rows page * 64 .. + 63 of the pool
+  constexpr int NQ = LD / 4;
+  uint32_t kq[8][NQ], vq[8][NQ], nkq[8][NQ], nvq[8][NQ];
+  float ksc[8], vsc[8], nksc[8], nvsc[8];
+  const int32_t* bt = block_tables + int64_t(b) * max_pages;
+  const uint32_t qlane_off = uint32_t(grp) * uint32_t(row_stride) + uint32_t(l16) * LD;
+  auto load_q = [&](uint32_t (&kd)[8][NQ], float (&ks)[8], uint32_t (&vd)[8][NQ], float (&vs)[8], int blk) {
+    const int64_t first = int64_t(blk) * KB + 32 * kh;
+    const int64_t left = L - first;
+    const uint32_t nv = uint32_t(left <= 0 ? 0 : (left < 32 ? left : 32));
+    const int64_t prow = int64_t(bt[min(blk, nblk - 1)]) * KB + 32 * kh;  // past the keys: any real page, nothing read
+    const int8_t* kb8 = static_cast<const int8_t*>(k_all) + prow * row_stride + g * D;
+    const int8_t* vb8 = static_cast<const int8_t*>(v_all) + prow * row_stride + g * D;
+    const __amdgpu_buffer_rsrc_t krs = buf_rsrc(wave_uniform(reinterpret_cast<const uint16_t*>(kb8)),
+                                                wave_uniform(nv * uint32_t(row_stride)));
+    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(wave_uniform(reinterpret_cast<const uint16_t*>(vb8)),
+                                                wave_uniform(nv * uint32_t(row_stride)));
+    const __amdgpu_buffer_rsrc_t kss = buf_rsrc(wave_uniform(reinterpret_cast<const uint16_t*>(k_scale + prow * Hkv + g)),
+                                                wave_uniform(nv * uint32_t(Hkv) * 4));
+    const __amdgpu_buffer_rsrc_t vss = buf_rsrc(wave_uniform(reinterpret_cast<const uint16_t*>(v_scale + prow * Hkv + g)),
+                                                wave_uniform(nv * uint32_t(Hkv) * 4));
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const uint32_t off = qlane_off + uint32_t(4 * it) * uint32_t(row_stride);
+      if constexpr (NQ == 2) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(krs, int(off), 0, 2);
+        kd[it][0] = v[0];
+        kd[it][1] = v[1];
+        const auto w = __builtin_amdgcn_raw_buffer_load_b64(vrs, int(off), 0, 2);
+        vd[it][0] = w[0];
+        vd[it][1] = w[1];
+      } else {
+        kd[it][0] = __builtin_amdgcn_raw_buffer_load_b32(krs, int(off), 0, 2);
+        vd[it][0] = __builtin_amdgcn_raw_buffer_load_b32(vrs, int(off), 0, 2);
+      }
+      const uint32_t soff = uint32_t(4 * it + grp) * uint32_t(Hkv) * 4;
+      ks[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kss, int(soff), 0, 0));
+      vs[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vss, int(soff), 0, 0));
+    }
+  };
+  // bf16(float(q) * scale) for the LD dims of one key, packed as NDW dwords
+  auto deq = [&](const uint32_t (&qd)[NQ], float sc, uint32_t (&out)[NDW]) {
+#pragma unroll
+    for (int c = 0; c < NDW; ++c) {
+      const uint32_t w = qd[c >> 1];
+      const int sh = 16 * (c & 1);
+      const float a = float(int8_t(w >> sh)) * sc;
+      const float bb = float(int8_t(w >> (sh + 8))) * sc;
+      out[c] = pack2bf(a, bb);
+    }
   };
 
   f32x4 oacc[LD];
@@ -177,10 +230,13 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
       const float tc = cs + __shfl_xor(cs, 32, 64);      // c0 + c2, c1 + c3
       const float rs = tc + __shfl_xor(tc, 16, 64);      // (c0 + c2) + (c1 + c3)
       l_run = __builtin_fmaf(l_run, alpha, rs);
+      // O's rows are heads 4 grp + r: each takes its own head's alpha (held by lane 4 grp + r)
 #pragma unroll
-      for (int e = 0; e < LD; ++e)
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * grp + r, 64);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[e][r] *= alpha;
+        for (int e = 0; e < LD; ++e) oacc[e][r] *= ar;
+      }
       // ---- O += P V: A = P (row head l16, k-slots 8 grp + j = class grp), B = V (col dim
       // LD l16 + e, same keys from the lane's own token-major registers)
       uint32_t h4[4], w4[4];
@@ -206,13 +262,33 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
 
   // two register sets, alternating, so the next block's loads are in flight
   // while a block is processed (past the request's keys the loads read zeros)
-  if (nb > 0) load(kw, vw, 0);
-  for (int blk = 0; blk < nb; blk += 2) {
-    load(nkw, nvw, blk + 1);
-    process(kw, vw, blk);
-    if (blk + 1 >= nb) break;
-    load(kw, vw, blk + 2);
-    process(nkw, nvw, blk + 1);
+  if constexpr (!Q8) {
+    if (nb > 0) load(kw, vw, 0);
+    for (int blk = 0; blk < nb; blk += 2) {
+      load(nkw, nvw, blk + 1);
+      process(kw, vw, blk);
+      if (blk + 1 >= nb) break;
+      load(kw, vw, blk + 2);
+      process(nkw, nvw, blk + 1);
+    }
+  } else {
+    auto process_q = [&](const uint32_t (&kd)[8][NQ], const float (&ks)[8], const uint32_t (&vd)[8][NQ],
+                         const float (&vs)[8], int blk) {
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        deq(kd[it], ks[it], kw[it]);
+        deq(vd[it], vs[it], vw[it]);
+      }
+      process(kw, vw, blk);
+    };
+    if (nb > 0) load_q(kq, ksc, vq, vsc, 0);
+    for (int blk = 0; blk < nb; blk += 2) {
+      load_q(nkq, nksc, nvq, nvsc, blk + 1);
+      process_q(kq, ksc, vq, vsc, blk);
+      if (blk + 1 >= nb) break;
+      load_q(kq, ksc, vq, vsc, blk + 2);
+      process_q(nkq, nksc, nvq, nvsc, blk + 1);
+    }
   }
 
   // ---- merge the halves (half 0, then half 1).  Lane (l16, grp) holds O of heads
@@ -254,13 +330,13 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
   }
 }
 
-template <int D, int G>
-hipError_t launch_t(const uint16_t* q, int64_t q_stride, const uint16_t* k_all, const uint16_t* v_all,
-                    const DecodeSeq* seqs, const int64_t* kv_offset, const int32_t* kv_len,
-                    const int32_t* order, int B, int64_t max_len, int Hkv, float sscale, uint16_t* o,
-                    int64_t o_stride, hipStream_t s) {
-  hipLaunchKernelGGL((decode_po_kernel<D, G>), dim3(Hkv, B), dim3(NT), 0, s, q, q_stride, k_all, v_all, seqs,
-                     kv_offset, kv_len, order, Hkv, max_len, sscale, o, o_stride);
+template <int D, int G, bool Q8>
+hipError_t launch_t(const uint16_t* q, int64_t q_stride, const void* k_all, const void* v_all, const float* ks,
+                    const float* vs, const int32_t* bt, int max_pages, const DecodeSeq* seqs, const int64_t* kv_offset,
+                    const int32_t* kv_len, const int32_t* order, int B, int64_t max_len, int Hkv, float sscale,
+                    uint16_t* o, int64_t o_stride, hipStream_t s) {
+  hipLaunchKernelGGL((decode_po_kernel<D, G, Q8>), dim3(Hkv, B), dim3(NT), 0, s, q, q_stride, k_all, v_all, ks, vs, bt,
+                     max_pages, seqs, kv_offset, kv_len, order, Hkv, max_len, sscale, o, o_stride);
   return hipGetLastError();
 }
 
@@ -273,10 +349,28 @@ hipError_t launch_attn_decode_po(const uint16_t* q, int64_t q_row_stride, const 
                                  hipStream_t s) {
   const float sscale = scale * 1.4426950408889634f;  // scores in log2 units, as prefill
   const int G = Hq / Hkv;
-#define BI_DPO(DD, GG)                                                                                   \
-  if (D == DD && G == GG)                                                                              \
-    return launch_t<DD, GG>(q, q_row_stride, k_all, v_all, d_seqs, kv_offset, kv_len, d_order, B, max_kv_len, \
-                            Hkv, sscale, o, o_row_stride, s);
+#define BI_DPO(DD, GG)                                                                                         \
+  if (D == DD && G == GG)                                                                                    \
+    return launch_t<DD, GG, false>(q, q_row_stride, k_all, v_all, nullptr, nullptr, nullptr, 0, d_seqs, kv_offset, \
+                                   kv_len, d_order, B, max_kv_len, Hkv, sscale, o, o_row_stride, s);
+  BI_DPO(64, 1) BI_DPO(64, 2) BI_DPO(64, 4) BI_DPO(64, 8)
+  BI_DPO(128, 1) BI_DPO(128, 2) BI_DPO(128, 4) BI_DPO(128, 8)
+#undef BI_DPO
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_decode_po_q8(const uint16_t* q, const int8_t* k_pool, const int8_t* v_pool,
+                                    const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                    int max_pages, const int32_t* kv_len, const int32_t* d_order, int B,
+                                    int64_t max_kv_len, int Hq, int Hkv, int D, float scale, uint16_t* o,
+                                    hipStream_t s) {
+  const float sscale = scale * 1.4426950408889634f;
+  const int G = Hq / Hkv;
+  const int64_t qs = int64_t(Hq) * D;
+#define BI_DPO(DD, GG)                                                                                          \
+  if (D == DD && G == GG)                                                                                     \
+    return launch_t<DD, GG, true>(q, qs, k_pool, v_pool, k_scale, v_scale, block_tables, max_pages, nullptr,      \
+                                  nullptr, kv_len, d_order, B, max_kv_len, Hkv, sscale, o, qs, s);
   BI_DPO(64, 1) BI_DPO(64, 2) BI_DPO(64, 4) BI_DPO(64, 8)
   BI_DPO(128, 1) BI_DPO(128, 2) BI_DPO(128, 4) BI_DPO(128, 8)
 #undef BI_DPO

@@ -26,9 +26,15 @@ pytestmark = pytest.mark.gpu
 LENS = np.array([1, 2, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 300, 1000, 2049])
 
 
-def packed_kv(lens, hkv, d, seed):
+def packed_kv(lens, hkv, d, seed, spread=0.0):
+    """Packed K/V ~ N(0,1); with spread > 0 every (key, head) row of K is scaled by
+    2^U(-spread, spread), so block maxima jump and the online softmax rescales often."""
     total = int(np.sum(lens))
     k = synth.normal_bf16_device(seed, (total, hkv, d))
+    if spread:
+        rng = np.random.default_rng(seed + 7)
+        mag = torch.from_numpy(np.exp2(rng.uniform(-spread, spread, (total, hkv, 1))).astype(np.float32)).cuda()
+        k = (k.float() * mag).to(torch.bfloat16)
     v = synth.normal_bf16_device(seed + 1, (total, hkv, d))
     offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
     return k, v, offs
@@ -41,12 +47,13 @@ def decode_po(q, k, v, offs, lens, max_len, hq, hkv, d, order=None):
         order=None if order is None else torch.from_numpy(np.asarray(order, np.int32)).cuda())
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (4, 4, 64), (8, 4, 128), (16, 4, 64)])
-def test_decode_equals_prefill_bitwise(hq, hkv, d):
+@pytest.mark.parametrize("hq,hkv,d,spread", [(32, 8, 128, 0.0), (4, 4, 64, 0.0), (8, 4, 128, 0.0), (16, 4, 64, 0.0),
+                                            (32, 8, 128, 8.0), (4, 4, 64, 3.0), (16, 4, 64, 6.0)])
+def test_decode_equals_prefill_bitwise(hq, hkv, d, spread):
     device()
     lens = LENS
-    announce("decode in prefill order vs prefill", hq, hkv, d)
-    k, v, offs = packed_kv(lens, hkv, d, 7000 + d + hq)
+    announce("decode in prefill order vs prefill", hq, hkv, d, spread)
+    k, v, offs = packed_kv(lens, hkv, d, 7000 + d + hq, spread)
     scale = 1.0 / math.sqrt(d)
     qs = [dev(synth.normal_bf16(7002 + 17 * b + hq, (int(L), hq * d))) for b, L in enumerate(lens)]
     q_last = torch.stack([qs[b][-1] for b in range(len(lens))])
@@ -63,12 +70,13 @@ def test_decode_equals_prefill_bitwise(hq, hkv, d):
         assert_bitwise(dec[b], draft[-1], f"L={L}: decode vs drafted chunk")
 
 
-def test_decode_prefill_order_parity():
+@pytest.mark.parametrize("spread", [0.0, 4.0])
+def test_decode_prefill_order_parity(spread):
     device()
     hq, hkv, d = 32, 8, 128
     lens = np.array([1, 33, 64, 97, 255, 1000, 4097])
-    announce("decode in prefill order parity", list(lens))
-    k, v, offs = packed_kv(lens, hkv, d, 7100)
+    announce("decode in prefill order parity", list(lens), spread)
+    k, v, offs = packed_kv(lens, hkv, d, 7100, spread)
     q = synth.normal_bf16(7102, (len(lens), hq * d))
     o = bits(decode_po(dev(q), k, v, offs, lens, int(lens.max()), hq, hkv, d))
     kb, vb = bits(k), bits(v)
