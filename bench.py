@@ -38,7 +38,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="mixed",
-                   choices=["mixed", "dense", "gemm", "decode", "norm", "tiny", "copy", "lmhead"])
+                   choices=["mixed", "dense", "gemm", "decode", "norm", "tiny", "copy", "lmhead", "decode_q8"])
     p.add_argument("--batch", type=int, default=256, help="decode requests in the mixed step")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-reps", type=int, default=10)
@@ -425,6 +425,55 @@ def run_lmhead(args, torch, bi, synth):
             "build_id": bi.build_id()}
 
 
+def run_decode_q8(args, torch, bi, synth):
+    """Decode over the quantised, paged cache for the mixed step's 256 requests (KV 513..8193,
+    32/8 heads x 128), in prefill key order, longest first; bf16 prefill-order decode on the same
+    requests beside it."""
+    import numpy as np
+    hq, hkv, d, B, PG = 32, 8, 128, 256, 64
+    lens = synth.uniform_ints(501, B, 512, 8192) + 1
+    npg = (lens + PG - 1) // PG
+    total_pages = int(npg.sum())
+    rng = np.random.default_rng(1400)
+    perm = rng.permutation(total_pages).astype(np.int32)
+    maxp = int(npg.max())
+    tables = np.zeros((B, maxp), np.int32)
+    used = 0
+    rows = []
+    for b in range(B):
+        tables[b, :npg[b]] = perm[used:used + npg[b]]
+        used += int(npg[b])
+        rows.append(tables[b, np.arange(lens[b]) // PG].astype(np.int64) * PG + np.arange(lens[b]) % PG)
+    rows = torch.from_numpy(np.concatenate(rows)).cuda()
+    pool = bi.KvPoolQ8(total_pages, hkv, d)
+    n = rows.numel()
+    for s0 in range(0, n, 1 << 18):        # quantise seeded bf16 keys and values into the pages
+        k = synth.normal_bf16_device(1401 + s0, (min(n - s0, 1 << 18), hkv, d))
+        v = synth.normal_bf16_device(1402 + s0, (min(n - s0, 1 << 18), hkv, d))
+        bi.kv_append_q8(pool, k, v, rows[s0:s0 + k.shape[0]].contiguous())
+    q = bi.to_dev(synth.normal_bf16(402, (B, hq * d)))
+    tbl = torch.from_numpy(tables).cuda()
+    ld = torch.from_numpy(lens.astype(np.int32)).cuda()
+    order = torch.from_numpy(np.argsort(-lens, kind="stable").astype(np.int32)).cuda()
+    out = torch.empty_like(q)
+    mx = int(lens.max())
+    t = event_time_ms(torch, lambda: bi.attn_decode_paged_q8(q, pool, tbl, ld, mx, hq, 1 / math.sqrt(d), order=order,
+                                                             out=out), max(args.kernel_reps, 20))
+    by = float(lens.sum()) * hkv * (d + 4) * 2
+    # the bf16 decode in prefill order on contiguous bf16 K/V of the same lengths
+    kb = synth.normal_bf16_device(403, (n, hkv, d))
+    vb = synth.normal_bf16_device(404, (n, hkv, d))
+    offs = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)).cuda()
+    t16 = event_time_ms(torch, lambda: bi.attn_decode_prefill_order(q, kb, vb, offs, ld, mx, hq, hkv, d,
+                                                                     1 / math.sqrt(d), order=order, out=out),
+                        max(args.kernel_reps, 20))
+    return {"metric": "decode attention GB/s (int8 paged cache, prefill key order)", "value": by / t / 1e6,
+            "unit": "GB/s", "ms": t, "frac": by / t / 1e6 / (PEAK_HBM / 1e9),
+            "bf16_same_requests": {"ms": t16, "gbs": float(lens.sum()) * hkv * d * 4 / t16 / 1e6},
+            "config": {"workload": "256 requests, KV 513..8193, 32/8 heads x 128, int8 codes + fp32 scale per "
+                                   "(token, head), 64-token pages in random order"}, "build_id": bi.build_id()}
+
+
 def run_copy(args, torch, bi, synth):
     """A plain 1 GiB device copy (torch), the reference for scaling HBM counters."""
     n = 1 << 29
@@ -448,7 +497,8 @@ def main():
         sys.exit(1)
     bi.lib()
     fn = {"mixed": run_mixed, "dense": run_dense, "gemm": run_gemm, "decode": run_decode,
-          "norm": run_norm, "tiny": run_tiny, "copy": run_copy, "lmhead": run_lmhead}[args.config]
+          "norm": run_norm, "tiny": run_tiny, "copy": run_copy, "lmhead": run_lmhead,
+          "decode_q8": run_decode_q8}[args.config]
     out = fn(args, torch, bi, synth)
     print(json.dumps(out), flush=True)
 

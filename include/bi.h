@@ -190,6 +190,43 @@ bi_status bi_attn_decode_prefill_order(const bi_bf16* q, const bi_bf16* k_all, c
                                        int Hq, int Hkv, int D, float scale, bi_bf16* o,
                                        hipStream_t stream);
 
+/* --------------------------------------------- quantised, paged KV cache
+ * The "Receipts" page ("What a receipt proves") lists a quantised cache among
+ * the load settings that decide the bits; the pages give no format.  Here:
+ * int8 codes, symmetric, one float32 scale per (token, kv head): with
+ * a = max |x_d| over the head, scale = a / 127, q_d = clamp(rint(x_d /
+ * scale), -127, 127) (IEEE fp32 division, ties to even; a = 0 stores zeros);
+ * attention reads bf16(float(q_d) * scale).  Pools are [rows, Hkv, D] int8
+ * codes and [rows, Hkv] float32 scales, in pages of 64 rows; a sequence's
+ * logical position p lives in row table[p / 64] * 64 + p % 64.  Everything a
+ * query computes is the bf16 kernels' arithmetic on the dequantised values,
+ * so results do not depend on page placement, batch or chunking.
+ * Page indices are not range-checked on the device: every index in a table
+ * must name a page of the pools.  D in {64, 128}.                            */
+
+/* Quantise rows of bf16 keys and values [rows, Hkv, D] into pool rows
+ * dst_row[r] (device int64 [rows]).                                          */
+bi_status bi_kv_append_q8(const bi_bf16* k, const bi_bf16* v, const int64_t* dst_row, int64_t rows,
+                          int Hkv, int D, int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
+                          hipStream_t stream);
+
+/* bi_attn_prefill over a paged int8 cache: block_table (device int32) holds
+ * at least ceil((q_start + T) / 64) page indices of the sequence.           */
+bi_status bi_attn_prefill_paged_q8(const bi_bf16* q, const int8_t* k_pool, const int8_t* v_pool,
+                                   const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                   bi_bf16* o, int64_t q_start, int64_t T, int Hq, int Hkv, int D,
+                                   float scale, hipStream_t stream);
+
+/* bi_attn_decode_prefill_order over a paged int8 cache (bitwise equal to
+ * bi_attn_prefill_paged_q8 for the same query): block_tables [B, max_pages]
+ * int32 device with max_pages >= ceil(max_kv_len / 64); kv_len, order, B,
+ * max_kv_len, o as there.                                                    */
+bi_status bi_attn_decode_paged_q8(const bi_bf16* q, const int8_t* k_pool, const int8_t* v_pool,
+                                  const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                  int max_pages, const int32_t* kv_len, const int32_t* order, int B,
+                                  int64_t max_kv_len, int Hq, int Hkv, int D, float scale, bi_bf16* o,
+                                  hipStream_t stream);
+
 /* ------------------------------------------------- the step after the block
  * Seeded sampling of the next token for each row of logits (after the final
  * RMSNorm, bi_rmsnorm, and the LM head, bi_gemm with N = vocabulary), and

@@ -86,6 +86,11 @@ _SIGNATURES = {
                                c_int, c_int, c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
     "bi_attn_decode_prefill_order": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                                              c_int64, c_int, c_int, c_int, c_float, c_void_p, c_void_p]),
+    "bi_kv_append_q8": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_void_p]),
+    "bi_attn_prefill_paged_q8": (c_int, [c_void_p] * 7 + [c_int64, c_int64, c_int, c_int, c_int, c_float, c_void_p]),
+    "bi_attn_decode_paged_q8": (c_int, [c_void_p] * 6 + [c_int, c_void_p, c_void_p, c_int, c_int64, c_int, c_int,
+                                                          c_int, c_float, c_void_p, c_void_p]),
     "bi_sample": (c_int, [c_void_p, c_int64, c_int64, ctypes.POINTER(bi_sampling), c_void_p, c_void_p, c_void_p,
                           c_int, c_void_p, c_void_p]),
     "bi_token_hash": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_void_p]),
@@ -264,6 +269,50 @@ def attn_decode_prefill_order(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq
     _check(lib().bi_attn_decode_prefill_order(_ptr(q), _ptr(k_all), _ptr(v_all), _ptr(kv_offset), _ptr(kv_len),
                                               _ptr(order), B, int(max_kv_len), Hq, Hkv, D, float(scale),
                                               _ptr(out), _stream()), "bi_attn_decode_prefill_order")
+    return out
+
+
+class KvPoolQ8:
+    """An int8 paged KV pool: codes [rows, Hkv, D] and float32 scales [rows, Hkv] for K and V."""
+
+    PAGE = 64
+
+    def __init__(self, pages, Hkv, D, device="cuda"):
+        rows = pages * self.PAGE
+        self.Hkv, self.D = Hkv, D
+        self.k = torch.zeros((rows, Hkv, D), dtype=torch.int8, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.ks = torch.zeros((rows, Hkv), dtype=torch.float32, device=device)
+        self.vs = torch.zeros_like(self.ks)
+
+
+def kv_append_q8(pool, k, v, dst_row):
+    """Quantise bf16 rows k, v [rows, Hkv, D] into pool rows dst_row (int64 device)."""
+    _dev(k, BF16, "k"); _dev(v, BF16, "v"); _dev(dst_row, torch.int64, "dst_row")
+    _check(lib().bi_kv_append_q8(_ptr(k), _ptr(v), _ptr(dst_row), k.shape[0], pool.Hkv, pool.D, _ptr(pool.k),
+                                 _ptr(pool.v), _ptr(pool.ks), _ptr(pool.vs), _stream()), "bi_kv_append_q8")
+
+
+def attn_prefill_paged_q8(q, pool, block_table, q_start, Hq, scale, out=None):
+    _dev(q, BF16, "q"); _dev(block_table, torch.int32, "block_table")
+    T = q.shape[0]
+    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_attn_prefill_paged_q8(_ptr(q), _ptr(pool.k), _ptr(pool.v), _ptr(pool.ks), _ptr(pool.vs),
+                                          _ptr(block_table), _ptr(out), int(q_start), T, Hq, pool.Hkv, pool.D,
+                                          float(scale), _stream()), "bi_attn_prefill_paged_q8")
+    return out
+
+
+def attn_decode_paged_q8(q, pool, block_tables, kv_len, max_kv_len, Hq, scale, order=None, out=None):
+    _dev(q, BF16, "q"); _dev(block_tables, torch.int32, "block_tables"); _dev(kv_len, torch.int32, "kv_len")
+    if order is not None:
+        _dev(order, torch.int32, "order")
+    B = q.shape[0]
+    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_attn_decode_paged_q8(_ptr(q), _ptr(pool.k), _ptr(pool.v), _ptr(pool.ks), _ptr(pool.vs),
+                                         _ptr(block_tables), block_tables.shape[1], _ptr(kv_len), _ptr(order), B,
+                                         int(max_kv_len), Hq, pool.Hkv, pool.D, float(scale), _ptr(out), _stream()),
+           "bi_attn_decode_paged_q8")
     return out
 
 

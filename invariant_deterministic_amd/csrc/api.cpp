@@ -346,6 +346,64 @@ bi_status bi_attn_decode_prefill_order(const bi_bf16* q, const bi_bf16* k_all, c
                                             stream));
 }
 
+bi_status bi_kv_append_q8(const bi_bf16* k, const bi_bf16* v, const int64_t* dst_row, int64_t rows, int Hkv,
+                          int D, int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
+                          hipStream_t stream) {
+  if (!k || !v || !dst_row || !k_pool || !v_pool || !k_scale || !v_scale) return BI_ERR_NULL;
+  if (rows < 1 || Hkv < 1) return BI_ERR_SHAPE;
+  if (rows > INT32_MAX || Hkv > 65535 || (D != 64 && D != 128)) return BI_ERR_UNSUPPORTED;
+  if (!aligned16(k) || !aligned16(v) || !aligned8(dst_row) || !aligned16(k_pool) || !aligned16(v_pool) ||
+      (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u))
+    return BI_ERR_ALIGN;
+  return from_hip(bi::launch_kv_quant(k, v, dst_row, rows, Hkv, D, k_pool, v_pool, k_scale, v_scale, stream));
+}
+
+bi_status bi_attn_prefill_paged_q8(const bi_bf16* q, const int8_t* k_pool, const int8_t* v_pool,
+                                   const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                   bi_bf16* o, int64_t q_start, int64_t T, int Hq, int Hkv, int D, float scale,
+                                   hipStream_t stream) {
+  if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !block_table || !o) return BI_ERR_NULL;
+  if (T < 1 || q_start < 0) return BI_ERR_SHAPE;
+  if (q_start + T > INT32_MAX) return BI_ERR_UNSUPPORTED;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
+  if (!head_shape_ok(Hq, Hkv, D, 4)) return BI_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return BI_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u))
+    return BI_ERR_ALIGN;
+  PrefillSeq one;
+  one.q_row = 0;
+  one.kv_base = 0;
+  one.q_start = int32_t(q_start);
+  one.q_len = int32_t(T);
+  const int P = bi::prefill_positions_per_tile(Hq / Hkv);
+  const int tiles = int((q_start + T - 1) / P - q_start / P + 1);
+  return from_hip(bi::launch_attn_prefill_q8(q, int64_t(Hq) * D, k_pool, v_pool, k_scale, v_scale, block_table, o,
+                                             int64_t(Hq) * D, &one, tiles, Hq, Hkv, D, scale, stream));
+}
+
+bi_status bi_attn_decode_paged_q8(const bi_bf16* q, const int8_t* k_pool, const int8_t* v_pool,
+                                  const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                  int max_pages, const int32_t* kv_len, const int32_t* order, int B,
+                                  int64_t max_kv_len, int Hq, int Hkv, int D, float scale, bi_bf16* o,
+                                  hipStream_t stream) {
+  if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !kv_len || !o) return BI_ERR_NULL;
+  if (B < 1 || max_kv_len < 1 || max_pages < 1) return BI_ERR_SHAPE;
+  if (B > 65535 || max_kv_len > (int64_t(1) << 30)) return BI_ERR_UNSUPPORTED;
+  if (int64_t(max_pages) * bi::kPrefillKeyBlock < max_kv_len) return BI_ERR_SHAPE;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
+  if (!head_shape_ok(Hq, Hkv, D, 8)) return BI_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return BI_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(kv_len) & 3u) ||
+      (reinterpret_cast<uintptr_t>(order) & 3u))
+    return BI_ERR_ALIGN;
+  return from_hip(bi::launch_attn_decode_po_q8(q, k_pool, v_pool, k_scale, v_scale, block_tables, max_pages, kv_len,
+                                               order, B, max_kv_len, Hq, Hkv, D, scale, o, stream));
+}
+
 bi_status bi_sample(const bi_bf16* logits, int64_t rows, int64_t vocab, const bi_sampling* params,
                     const uint64_t* seeds, const int64_t* positions, const int32_t* history, int n_hist,
                     int32_t* out_ids, hipStream_t stream) {

@@ -119,11 +119,9 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
   // int8 paged cache: LD codes per key (NQ dwords) and the key's scale; block blk is page
   // block_tables[b][blk], rows page * 64 .. + 63 of the pool
   constexpr int NQ = LD / 4;
-  uint32_t kq[8][NQ], vq[8][NQ], nkq[8][NQ], nvq[8][NQ];
-  float ksc[8], vsc[8], nksc[8], nvsc[8];
   const int32_t* bt = block_tables + int64_t(b) * max_pages;
   const uint32_t qlane_off = uint32_t(grp) * uint32_t(row_stride) + uint32_t(l16) * LD;
-  auto load_q = [&](uint32_t (&kd)[8][NQ], float (&ks)[8], uint32_t (&vd)[8][NQ], float (&vs)[8], int blk) {
+  auto load_q = [&](uint32_t (&kd)[8][NQ], float& ks, uint32_t (&vd)[8][NQ], float& vs, int blk) {
     const int64_t first = int64_t(blk) * KB + 32 * kh;
     const int64_t left = L - first;
     const uint32_t nv = uint32_t(left <= 0 ? 0 : (left < 32 ? left : 32));
@@ -152,22 +150,14 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
         kd[it][0] = __builtin_amdgcn_raw_buffer_load_b32(krs, int(off), 0, 2);
         vd[it][0] = __builtin_amdgcn_raw_buffer_load_b32(vrs, int(off), 0, 2);
       }
-      const uint32_t soff = uint32_t(4 * it + grp) * uint32_t(Hkv) * 4;
-      ks[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kss, int(soff), 0, 0));
-      vs[it] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vss, int(soff), 0, 0));
     }
+    // lane holds the scale of key (lane mod 32) of the half; the lanes that need it read it by a shuffle
+    const uint32_t soff = uint32_t(lane & 31) * uint32_t(Hkv) * 4;
+    ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(kss, int(soff), 0, 0));
+    vs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(vss, int(soff), 0, 0));
   };
-  // bf16(float(q) * scale) for the LD dims of one key, packed as NDW dwords
-  auto deq = [&](const uint32_t (&qd)[NQ], float sc, uint32_t (&out)[NDW]) {
-#pragma unroll
-    for (int c = 0; c < NDW; ++c) {
-      const uint32_t w = qd[c >> 1];
-      const int sh = 16 * (c & 1);
-      const float a = float(int8_t(w >> sh)) * sc;
-      const float bb = float(int8_t(w >> (sh + 8))) * sc;
-      out[c] = pack2bf(a, bb);
-    }
-  };
+  // bf16(float(code) * scale): code b of a dword
+  auto dq = [](uint32_t w, int b, float sc) { return float(int8_t(w >> (8 * b))) * sc; };
 
   f32x4 oacc[LD];
 #pragma unroll
@@ -177,7 +167,8 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
   const int rr = 4 * (l16 & 3) + (l16 >> 2);  // K tile row read as MFMA row l16
 
   // per block: scores, online softmax and value product of this wave's half
-  auto process = [&](const uint32_t (&kd)[8][NDW], const uint32_t (&vd)[8][NDW], int blk) {
+  // kword(it, c): dword c (two bf16) of key it's K slice; vpair(jj, e): dim e of keys 2 jj, 2 jj + 1
+  auto process = [&](auto&& kword, auto&& vpair, int blk) {
       // ---- scores: two 16-key tiles; tile row 4 j + grp holds key 4 (4 kb + j) + grp, so
       // output register r of lane (head l16, grp) is key 4 (4 kb + r) + grp
       f32x4 sacc[2];
@@ -186,13 +177,14 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kr = 4 * j + grp;
-          const uint32_t* src = kd[4 * kb + j];
+          const int it = 4 * kb + j;
           if constexpr (NDW == 4) {
             const int phys = l16 ^ (kr & (NG - 1));
-            *reinterpret_cast<uint4*>(sk + kr * D + phys * 8) = make_uint4(src[0], src[1], src[2], src[3]);
+            *reinterpret_cast<uint4*>(sk + kr * D + phys * 8) =
+                make_uint4(kword(it, 0), kword(it, 1), kword(it, 2), kword(it, 3));
           } else {
             const int phys = (l16 >> 1) ^ (kr & (NG - 1));
-            *reinterpret_cast<uint2*>(sk + kr * D + phys * 8 + (l16 & 1) * 4) = make_uint2(src[0], src[1]);
+            *reinterpret_cast<uint2*>(sk + kr * D + phys * 8 + (l16 & 1) * 4) = make_uint2(kword(it, 0), kword(it, 1));
           }
         }
         sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -250,11 +242,7 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
       const bf16x8 pl = as_bf16x8(make_uint4(w4[0], w4[1], w4[2], w4[3]));
 #pragma unroll
       for (int e = 0; e < LD; ++e) {
-        uint32_t vt[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          vt[jj] = __builtin_amdgcn_perm(vd[2 * jj + 1][e >> 1], vd[2 * jj][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-        const bf16x8 vb = as_bf16x8(make_uint4(vt[0], vt[1], vt[2], vt[3]));
+        const bf16x8 vb = as_bf16x8(make_uint4(vpair(0, e), vpair(1, e), vpair(2, e), vpair(3, e)));
         oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[e], 0, 0, 0);
         oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[e], 0, 0, 0);
       }
@@ -263,31 +251,51 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
   // two register sets, alternating, so the next block's loads are in flight
   // while a block is processed (past the request's keys the loads read zeros)
   if constexpr (!Q8) {
+    auto run = [&](const uint32_t (&kd)[8][NDW], const uint32_t (&vd)[8][NDW], int blk) {
+      process([&](int it, int c) { return kd[it][c]; },
+              [&](int jj, int e) {
+                return __builtin_amdgcn_perm(vd[2 * jj + 1][e >> 1], vd[2 * jj][e >> 1],
+                                             (e & 1) ? 0x07060302u : 0x05040100u);
+              },
+              blk);
+    };
     if (nb > 0) load(kw, vw, 0);
     for (int blk = 0; blk < nb; blk += 2) {
       load(nkw, nvw, blk + 1);
-      process(kw, vw, blk);
+      run(kw, vw, blk);
       if (blk + 1 >= nb) break;
       load(kw, vw, blk + 2);
-      process(nkw, nvw, blk + 1);
+      run(nkw, nvw, blk + 1);
     }
   } else {
-    auto process_q = [&](const uint32_t (&kd)[8][NQ], const float (&ks)[8], const uint32_t (&vd)[8][NQ],
-                         const float (&vs)[8], int blk) {
+    // int8 codes dequantised where they are consumed: K while the K tile is written, V while
+    // the value operand is built (the same bf16(float(code) * scale) values throughout)
+    auto run_q = [&](const uint32_t (&kd)[8][NQ], float ksr, const uint32_t (&vd)[8][NQ], float vsr, int blk) {
+      float ks[8], vs[8];
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        deq(kd[it], ks[it], kw[it]);
-        deq(vd[it], vs[it], vw[it]);
+        ks[it] = __shfl(ksr, 4 * it + grp, 64);
+        vs[it] = __shfl(vsr, 4 * it + grp, 64);
       }
-      process(kw, vw, blk);
+      process([&](int it, int c) {
+                const uint32_t w = kd[it][c >> 1];
+                const int b0 = 2 * (c & 1);
+                return pack2bf(dq(w, b0, ks[it]), dq(w, b0 + 1, ks[it]));
+              },
+              [&](int jj, int e) {
+                return pack2bf(dq(vd[2 * jj][e >> 2], e & 3, vs[2 * jj]), dq(vd[2 * jj + 1][e >> 2], e & 3, vs[2 * jj + 1]));
+              },
+              blk);
     };
-    if (nb > 0) load_q(kq, ksc, vq, vsc, 0);
+    uint32_t kq[8][NQ], vq[8][NQ], nkq[8][NQ], nvq[8][NQ];
+    float ksr = 0.f, vsr = 0.f, nksr = 0.f, nvsr = 0.f;
+    if (nb > 0) load_q(kq, ksr, vq, vsr, 0);
     for (int blk = 0; blk < nb; blk += 2) {
-      load_q(nkq, nksc, nvq, nvsc, blk + 1);
-      process_q(kq, ksc, vq, vsc, blk);
+      load_q(nkq, nksr, nvq, nvsr, blk + 1);
+      run_q(kq, ksr, vq, vsr, blk);
       if (blk + 1 >= nb) break;
-      load_q(kq, ksc, vq, vsc, blk + 2);
-      process_q(nkq, nksc, nvq, nvsc, blk + 1);
+      load_q(kq, ksr, vq, vsr, blk + 2);
+      run_q(nkq, nksr, nvq, nvsr, blk + 1);
     }
   }
 

@@ -94,10 +94,11 @@ __device__ __forceinline__ int key_at_pos(int pos) {
   return (pos & 32) | ((pos & 7) << 2) | ((pos >> 3) & 3);
 }
 
-template <int D, int G>
+template <int D, int G, bool Q8>
 __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
-    const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, uint16_t* __restrict__ o, int64_t o_stride,
+    const uint16_t* __restrict__ q, int64_t q_stride, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    const int32_t* __restrict__ pages, uint16_t* __restrict__ o, int64_t o_stride,
     const PrefillSeq* __restrict__ seqs, PrefillSeq single, int Hkv, float sscale, int fold) {
   constexpr int R = NW / (2 * G);     // 32-position groups per tile
   constexpr int P = QW * R;           // positions per tile
@@ -138,24 +139,58 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
   const int ur = u / DCH;
   // head g's slice of the sequence's cache rows; the lane's 16-byte chunk uc
   // goes into the per-lane buffer offset
-  const uint16_t* kbase = k_cache + sq.kv_base * kv_stride + int64_t(g) * D;
-  const uint16_t* vbase = v_cache + sq.kv_base * kv_stride + int64_t(g) * D;
+  const uint16_t* kbase = static_cast<const uint16_t*>(k_cache) + sq.kv_base * kv_stride + int64_t(g) * D;
+  const uint16_t* vbase = static_cast<const uint16_t*>(v_cache) + sq.kv_base * kv_stride + int64_t(g) * D;
   uint4 rr[KPT];
+  uint2 rq[KPT];   // int8 cache: 8 codes of the chunk, and the key's scale
+  float rsc[KPT];
   // block blk as a buffer over its valid keys (keys >= kv_valid read as zero)
   auto load_block = [&](int blk) {
     const int nvalid = min(KB, max(0, kv_valid - blk * KB));
-    // K or V is chosen per wave (the first HT threads move K)
-    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(wave_uniform((is_k ? kbase : vbase) + int64_t(blk) * KB * kv_stride),
-                                               wave_uniform(uint32_t(nvalid) * uint32_t(kv_stride) * 2));
+    if constexpr (!Q8) {
+      // K or V is chosen per wave (the first HT threads move K)
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(wave_uniform((is_k ? kbase : vbase) + int64_t(blk) * KB * kv_stride),
+                                                 wave_uniform(uint32_t(nvalid) * uint32_t(kv_stride) * 2));
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int key = is_k ? ur + (HT / DCH) * i : key_at_pos(KPT * ur + i);
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
-          rs, int(uint32_t(key) * uint32_t(kv_stride) * 2 + uint32_t(uc) * 16), 0, 0);
-      rr[i] = make_uint4(v.x, v.y, v.z, v.w);
+      for (int i = 0; i < KPT; ++i) {
+        const int key = is_k ? ur + (HT / DCH) * i : key_at_pos(KPT * ur + i);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(
+            rs, int(uint32_t(key) * uint32_t(kv_stride) * 2 + uint32_t(uc) * 16), 0, 0);
+        rr[i] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    } else {
+      // block blk is page pages[blk]: rows pages[blk] * 64 .. + 63 of the int8 pool
+      const int64_t prow = int64_t(pages[blk]) * KB;
+      const int8_t* qb = static_cast<const int8_t*>(is_k ? k_cache : v_cache) + prow * kv_stride + int64_t(g) * D;
+      const float* sb = (is_k ? k_scale : v_scale) + prow * Hkv + g;
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(wave_uniform(reinterpret_cast<const uint16_t*>(qb)),
+                                                 wave_uniform(uint32_t(nvalid) * uint32_t(kv_stride)));
+      const __amdgpu_buffer_rsrc_t ss = buf_rsrc(wave_uniform(reinterpret_cast<const uint16_t*>(sb)),
+                                                 wave_uniform(uint32_t(nvalid) * uint32_t(Hkv) * 4));
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int key = is_k ? ur + (HT / DCH) * i : key_at_pos(KPT * ur + i);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, int(uint32_t(key) * uint32_t(kv_stride) + uint32_t(uc) * 8), 0, 0);
+        rq[i] = make_uint2(v[0], v[1]);
+        rsc[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ss, int(uint32_t(key) * uint32_t(Hkv) * 4), 0, 0));
+      }
     }
   };
+  // int8 codes of a chunk -> bf16(float(q) * scale), 8 values
+  auto dequant = [&](int i) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = e < 4 ? rq[i].x : rq[i].y;
+      f[e] = float(int8_t(w >> (8 * (e & 3)))) * rsc[i];
+    }
+    rr[i] = pack8(f);
+  };
   auto store_block = [&](int stage) {
+    if constexpr (Q8) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) dequant(i);
+    }
     if (is_k) {
 #pragma unroll
       for (int i = 0; i < KPT; ++i)
@@ -375,10 +410,10 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
   if (fold && x < ta) do_tile(first_tile + x);
 }
 
-template <int D, int G>
-hipError_t launch_t(const uint16_t* q, int64_t q_stride, const uint16_t* k, const uint16_t* v,
-                    uint16_t* o, int64_t o_stride, const PrefillSeq* seqs, PrefillSeq single,
-                    int n_seqs, int max_tiles, int Hkv, float sscale, hipStream_t s) {
+template <int D, int G, bool Q8>
+hipError_t launch_t(const uint16_t* q, int64_t q_stride, const void* k, const void* v, const float* ks,
+                    const float* vs, const int32_t* pages, uint16_t* o, int64_t o_stride, const PrefillSeq* seqs,
+                    PrefillSeq single, int n_seqs, int max_tiles, int Hkv, float sscale, hipStream_t s) {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0;
@@ -388,8 +423,8 @@ hipError_t launch_t(const uint16_t* q, int64_t q_stride, const uint16_t* k, cons
   }
   const int fold = int64_t(max_tiles) * Hkv * n_seqs > cus ? 1 : 0;
   const int gx = fold ? (max_tiles + 1) / 2 : max_tiles;
-  hipLaunchKernelGGL((prefill_kernel<D, G>), dim3(gx, Hkv, n_seqs), dim3(NTH), 0, s, q, q_stride, k, v, o,
-                     o_stride, seqs, single, Hkv, sscale, fold);
+  hipLaunchKernelGGL((prefill_kernel<D, G, Q8>), dim3(gx, Hkv, n_seqs), dim3(NTH), 0, s, q, q_stride, k, v, ks, vs,
+                     pages, o, o_stride, seqs, single, Hkv, sscale, fold);
   return hipGetLastError();
 }
 
@@ -405,10 +440,27 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t q_row_stride, const ui
   if (h_single) single = *h_single;
   const int G = Hq / Hkv;
   const float sscale = scale * 1.4426950408889634f;
-#define BI_PF(DD, GG)                                                                          \
-  if (D == DD && G == GG)                                                                    \
-    return launch_t<DD, GG>(q, q_row_stride, k_cache, v_cache, o, o_row_stride, d_seqs, single, \
-                            n_seqs, max_tiles, Hkv, sscale, s);
+#define BI_PF(DD, GG)                                                                                    \
+  if (D == DD && G == GG)                                                                              \
+    return launch_t<DD, GG, false>(q, q_row_stride, k_cache, v_cache, nullptr, nullptr, nullptr, o, o_row_stride, \
+                                   d_seqs, single, n_seqs, max_tiles, Hkv, sscale, s);
+  BI_PF(64, 1) BI_PF(64, 2) BI_PF(64, 4)
+  BI_PF(128, 1) BI_PF(128, 2) BI_PF(128, 4)
+#undef BI_PF
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_prefill_q8(const uint16_t* q, int64_t q_row_stride, const int8_t* k_pool, const int8_t* v_pool,
+                                  const float* k_scale, const float* v_scale, const int32_t* pages, uint16_t* o,
+                                  int64_t o_row_stride, const PrefillSeq* h_single, int max_tiles, int Hq, int Hkv,
+                                  int D, float scale, hipStream_t s) {
+  const PrefillSeq single = *h_single;
+  const int G = Hq / Hkv;
+  const float sscale = scale * 1.4426950408889634f;
+#define BI_PF(DD, GG)                                                                                    \
+  if (D == DD && G == GG)                                                                              \
+    return launch_t<DD, GG, true>(q, q_row_stride, k_pool, v_pool, k_scale, v_scale, pages, o, o_row_stride, \
+                                  nullptr, single, 1, max_tiles, Hkv, sscale, s);
   BI_PF(64, 1) BI_PF(64, 2) BI_PF(64, 4)
   BI_PF(128, 1) BI_PF(128, 2) BI_PF(128, 4)
 #undef BI_PF

@@ -84,6 +84,20 @@ hipError_t launch_attn_decode_po(const uint16_t* q, int64_t q_row_stride, const 
                                  int Hq, int Hkv, int D, float scale, uint16_t* o, int64_t o_row_stride,
                                  hipStream_t s);
 
+// Quantised, paged KV cache: int8 codes [rows, Hkv, D] with float32 scales
+// [rows, Hkv]; pages of 64 rows; page tables are int32.
+hipError_t launch_kv_quant(const uint16_t* k, const uint16_t* v, const int64_t* dst_row, int64_t rows, int Hkv,
+                           int D, int8_t* kq, int8_t* vq, float* ks, float* vs, hipStream_t s);
+hipError_t launch_attn_prefill_q8(const uint16_t* q, int64_t q_row_stride, const int8_t* k_pool, const int8_t* v_pool,
+                                  const float* k_scale, const float* v_scale, const int32_t* pages, uint16_t* o,
+                                  int64_t o_row_stride, const PrefillSeq* h_single, int max_tiles, int Hq, int Hkv,
+                                  int D, float scale, hipStream_t s);
+hipError_t launch_attn_decode_po_q8(const uint16_t* q, const int8_t* k_pool, const int8_t* v_pool,
+                                    const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                                    int max_pages, const int32_t* kv_len, const int32_t* d_order, int B,
+                                    int64_t max_kv_len, int Hq, int Hkv, int D, float scale, uint16_t* o,
+                                    hipStream_t s);
+
 // Sampler settings (mirrors bi_sampling of the public header).
 struct BiSampling {
   float temperature;
