@@ -9,6 +9,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <utility>
+#include <vector>
 
 #include <hip/hip_vector_types.h>
 
@@ -67,28 +69,30 @@ bool scale_ok(float s) { return s > 0.f && s < 3.0e38f; }
 
 // ---- step metadata layout (host bytes uploaded by the caller)
 struct MetaLayout {
-  size_t prefill, decode, pos, kv, units, order, total;
+  size_t prefill, decode, pos, kv, runs, order, total;
 };
 // Layout of the packed step description: header, prefill descriptors, decode
-// descriptors, per-row positions, per-row KV rows, the decode unit list
-// (one (request, unit) int32 pair per 256 keys of each decode request), then
-// the decode requests ordered longest first (int32 indices).
-MetaLayout meta_layout(int n_seqs, int64_t n_tokens, int64_t n_units) {
+// descriptors, per-row positions, per-row KV rows, the split decode's run list
+// (one (request, first unit) int32 pair per run of up to kDecodeRun 256-key
+// units, longest runs first), then the decode requests ordered longest first
+// (int32 indices).
+MetaLayout meta_layout(int n_seqs, int64_t n_tokens, int64_t n_runs) {
   MetaLayout L;
   L.prefill = 256;
   L.decode = L.prefill + align256(size_t(n_seqs) * sizeof(PrefillSeq));
   L.pos = L.decode + align256(size_t(n_seqs) * sizeof(DecodeSeq));
   L.kv = L.pos + align256(size_t(n_tokens) * sizeof(int32_t));
-  L.units = L.kv + align256(size_t(n_tokens) * sizeof(int64_t));
-  L.order = L.units + align256(size_t(n_units) * 8);
+  L.runs = L.kv + align256(size_t(n_tokens) * sizeof(int64_t));
+  L.order = L.runs + align256(size_t(n_runs) * 8);
   L.total = L.order + align256(size_t(n_seqs) * sizeof(int32_t));
   return L;
 }
-int64_t decode_units(const bi_seq* seqs, int n_seqs) {
-  int64_t u = 0;
+int64_t units_of(int64_t kv_len) { return (kv_len + bi::kKvSplit - 1) / bi::kKvSplit; }
+int64_t decode_runs(const bi_seq* seqs, int n_seqs) {
+  int64_t r = 0;
   for (int i = 0; i < n_seqs; ++i)
-    if (seqs[i].q_len == 1) u += (int64_t(seqs[i].ctx_len) + 1 + bi::kKvSplit - 1) / bi::kKvSplit;
-  return u;
+    if (seqs[i].q_len == 1) r += (units_of(int64_t(seqs[i].ctx_len) + 1) + bi::kDecodeRun - 1) / bi::kDecodeRun;
+  return r;
 }
 
 struct StepSummary {
@@ -449,7 +453,7 @@ bi_status bi_token_hash(const int32_t* ids, const int64_t* offsets, const int32_
 size_t bi_step_meta_bytes(const bi_seq* seqs, int n_seqs) {
   StepSummary s;
   if (summarize(seqs, n_seqs, &s) != BI_OK) return 0;
-  return meta_layout(n_seqs, s.M, decode_units(seqs, n_seqs)).total;
+  return meta_layout(n_seqs, s.M, decode_runs(seqs, n_seqs)).total;
 }
 
 bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t bytes) {
@@ -457,9 +461,9 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
   bi_status st = summarize(seqs, n_seqs, &s);
   if (st != BI_OK) return st;
   if (!host_meta) return BI_ERR_NULL;
-  const int64_t n_units = decode_units(seqs, n_seqs);
-  if (n_units > INT32_MAX) return BI_ERR_UNSUPPORTED;
-  const MetaLayout L = meta_layout(n_seqs, s.M, n_units);
+  const int64_t n_runs = decode_runs(seqs, n_seqs);
+  if (n_runs > INT32_MAX) return BI_ERR_UNSUPPORTED;
+  const MetaLayout L = meta_layout(n_seqs, s.M, n_runs);
   if (bytes < L.total) return BI_ERR_WORKSPACE;
   memset(host_meta, 0, L.total);
   int64_t* hdr = at<int64_t>(host_meta, 0);
@@ -467,8 +471,8 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
   hdr[1] = s.M;
   hdr[2] = s.n_prefill;
   hdr[3] = s.n_decode;
-  hdr[4] = n_units;
-  int32_t* units = at<int32_t>(host_meta, L.units);
+  hdr[4] = n_runs;
+  int32_t* runs = at<int32_t>(host_meta, L.runs);
   int64_t u = 0;
   PrefillSeq* pf = at<PrefillSeq>(host_meta, L.prefill);
   DecodeSeq* dc = at<DecodeSeq>(host_meta, L.decode);
@@ -484,10 +488,10 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
       d.kv_offset = q.kv_base;
       d.kv_len = q.ctx_len + 1;
       d.pad = 0;
-      const int64_t nu = (int64_t(d.kv_len) + bi::kKvSplit - 1) / bi::kKvSplit;
-      for (int64_t k = 0; k < nu; ++k, ++u) {
-        units[2 * u] = nd;
-        units[2 * u + 1] = int32_t(k);
+      const int64_t nu = units_of(d.kv_len);
+      for (int64_t k = 0; k < nu; k += bi::kDecodeRun, ++u) {
+        runs[2 * u] = nd;
+        runs[2 * u + 1] = int32_t(k);
       }
       dc[nd++] = d;
     } else {
@@ -503,6 +507,19 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
       kvr[row + j] = q.kv_base + q.ctx_len + j;
     }
     row += q.q_len;
+  }
+  // runs with the most units first (ties in list order): only the launch order
+  {
+    std::vector<std::pair<int32_t, int32_t>> rl(static_cast<size_t>(n_runs));
+    for (int64_t i = 0; i < n_runs; ++i) rl[size_t(i)] = {runs[2 * i], runs[2 * i + 1]};
+    auto run_units = [&](const std::pair<int32_t, int32_t>& r) {
+      return std::min<int64_t>(bi::kDecodeRun, units_of(dc[r.first].kv_len) - r.second);
+    };
+    std::stable_sort(rl.begin(), rl.end(), [&](const auto& a, const auto& b) { return run_units(a) > run_units(b); });
+    for (int64_t i = 0; i < n_runs; ++i) {
+      runs[2 * i] = rl[size_t(i)].first;
+      runs[2 * i + 1] = rl[size_t(i)].second;
+    }
   }
   // decode requests longest first (ties by index): only the launch order
   int32_t* order = at<int32_t>(host_meta, L.order);
@@ -557,9 +574,9 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
   const int64_t M = s.M;
   const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, F = c.ffn;
   const int qkv_n = (Hq + 2 * Hkv) * D;
-  const int64_t n_units = decode_units(seqs, n_seqs);
-  if (n_units > INT32_MAX) return BI_ERR_UNSUPPORTED;
-  const MetaLayout ML = meta_layout(n_seqs, M, n_units);
+  const int64_t n_runs = decode_runs(seqs, n_seqs);
+  if (n_runs > INT32_MAX) return BI_ERR_UNSUPPORTED;
+  const MetaLayout ML = meta_layout(n_seqs, M, n_runs);
   uint16_t* n1 = at<uint16_t>(ws, L.pub.n1);
   uint16_t* qkv = at<uint16_t>(ws, L.pub.qkv);
   uint16_t* q = at<uint16_t>(ws, L.pub.q);
@@ -597,7 +614,7 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
                                      s.max_decode_len, Hq, Hkv, D, scale, attn, int64_t(Hq) * D, stream));
   } else if (s.n_decode) {
     BI_TRY(bi::launch_attn_decode(q, int64_t(Hq) * D, kv->k, kv->v, at<DecodeSeq>(d_meta, ML.decode),
-                                  at<int2>(d_meta, ML.units), int(n_units), s.n_decode,
+                                  at<int2>(d_meta, ML.runs), int(n_runs), s.n_decode,
                                   s.max_decode_len, Hq, Hkv, D, scale,
                                   at<void>(ws, L.pub.decode_partials), attn, int64_t(Hq) * D,
                                   stream));

@@ -5,36 +5,46 @@
 // axis into pieces of a fixed *size* rather than into a fixed *number* of
 // pieces.  Here the piece is 256 keys: request b with L_b keys has
 // ceil(L_b / 256) units, unit s covering keys [256 s, min(256 s + 256, L_b)).
-// How a unit is reduced depends only on its keys, and the units of a request
-// are merged in ascending s by a second kernel, so a request's bits never
-// depend on the batch, the other requests' lengths or the grid.
+// The pieces are reduced and merged in a tree whose shape depends only on
+// L_b: each unit on its own, then runs of 8 consecutive units (units
+// 8 r .. 8 r + 7 form run r) merged in ascending unit order, then the runs
+// merged in ascending order.  A request's bits therefore never depend on the
+// batch, the other requests' lengths, the launch order or the grid.
 //
-// Split kernel: one 512-thread work-group per (kv head g, unit s, request b)
-// (the block entry point passes a host-built list of the step's real units,
-// the standalone one launches the max-units grid and idle groups exit), for
-// the G query heads sharing kv head g; 8 waves, each owning 32 of the keys.
+// Unit kernel: one 2-wave work-group per (run r of request b, kv head g), for
+// the G query heads sharing kv head g (the block entry point passes a
+// host-built list of the step's runs, those with the most units first; the
+// standalone one builds the same list on the device).  A unit is 4 blocks of
+// 64 keys; wave kh takes keys 32 kh .. 32 kh + 31 of every block.
 //   loads   token-major: a lane takes 16 bytes (D/16 dims) of one key row, so
 //           each load instruction covers four whole head rows; raw buffer
 //           loads bounded at the request's last key read zero past it, with no
-//           branch.  The query rows go once through LDS.
+//           branch.  Two register sets alternate, so the next block (also
+//           across a unit's end) is in flight while one is reduced.
 //   scores  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (D/32 k-steps in ascending
-//           order), K passed through a per-wave LDS block of 16 keys to reach
-//           the operand layout, times scale * log2(e).  The block's row order
-//           is chosen so that each lane ends up holding the scores of the very
-//           keys whose values it loaded.
-//   m       exact maximum over the unit (order-free);
-//   p       exp2(score - m); l = sum of p (fixed in-lane order, lane pairs
-//           16 and 32 apart, then waves 0..7);
-//   o       P V on v_mfma_f32_16x16x32_bf16: the value operand is the lane's own
-//           token-major registers regrouped by byte permutes (eight keys of one
-//           dim), P enters as a bf16 high part plus a bf16 remainder; the 8
-//           waves' partials are added in ascending order through LDS.
-// Partials (m, l, o[D]) go to the workspace in fp32.  Keys past L_b contribute
-// score -inf, p = 0 and value 0.
-//
-// Combine kernel: one thread per (request, head, dim) walks s = 0 .. S_b - 1
-// in ascending order: M = max m_s; w_s = exp2(m_s - M); O = sum w_s o_s,
-// Lsum = sum w_s l_s; output bf16(O / Lsum).
+//           order), K passed through a per-wave LDS tile of 16 keys to reach
+//           the operand layout, times scale * log2(e); keys past L_b -inf.
+//   softmax online per wave over its 32-key halves, from a fresh state at each
+//           unit: the reference maximum m moves only when a block's maximum
+//           exceeds it by more than 8; alpha = exp2(m - m_new), p = exp2(score
+//           - m_new), l = fma(l, alpha, rowsum) with the rowsum in a fixed
+//           in-lane and lane-pair order, O *= alpha (each output row by its
+//           own head's alpha);
+//   o       P V on v_mfma_f32_16x16x32_bf16: the value operand is the lane's
+//           own token-major registers regrouped by byte permutes (eight keys
+//           of one dim), P enters as a bf16 high part plus a bf16 remainder.
+//   unit    the halves merge through LDS: m = max(m0, m1), a_i = exp2(m_i -
+//           m), l = fma(l0, a0, l1 a1), o = fma(O0, a0, O1 a1); the unit's
+//           (m, l, o) stays in LDS.
+//   run     at the run's end its units merge in ascending order with the
+//           formula below; the run's (m, l, o[D]) goes to the workspace in
+//           fp32 (one record per 2048 keys and head: partial sums are a small
+//           fraction of the bytes moved, which keeps HBM on the key/value
+//           stream).
+// Merge of pieces 0 .. S - 1 (units of a run, then runs of a request):
+// M = max m_s; w_s = exp2(m_s - M); O = sum w_s o_s and Lsum = sum w_s l_s
+// as fmas in ascending s.  The combine kernel, one thread per (request, head,
+// dim), merges the runs and writes bf16(O / Lsum).
 #include "bi_dev.h"
 #include "bi_internal.h"
 
@@ -42,201 +52,271 @@ namespace bi {
 namespace {
 
 constexpr int kSplit = kKvSplit;      // 256 keys per unit
-constexpr int kWavesPerUnit = 8;      // 32 keys per wave
-constexpr int kKeysPerWave = kSplit / kWavesPerUnit;
-constexpr int kSplitThreads = 64 * kWavesPerUnit;
+constexpr int KB = 64;                // keys per block; a unit is 4 blocks
+constexpr int kUnitBlocks = kSplit / KB;
+constexpr int NT = 128;               // two waves: key halves
 
+// One work-group per (run list entry blockIdx.x = (request b, first unit u0), kv head
+// blockIdx.y); entries at or past *n_runs (when given) have nothing to do.
 template <int D, int G>
-__global__ __launch_bounds__(kSplitThreads) void decode_split_kernel(
+__global__ __launch_bounds__(NT) void decode_unit_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_all,
     const uint16_t* __restrict__ v_all, const DecodeSeq* __restrict__ seqs,
-    const int2* __restrict__ units, int Hkv, int64_t max_len, int max_splits, float qscale,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
-  constexpr int LD = D / 16;              // dims per lane in the token-major loads
-  constexpr int NDW = LD / 2;             // their dwords
-  constexpr int KS = D / 32;              // MFMA k-steps over the head dimension
-  constexpr int NG = D / 8;               // 16-byte granules per key row
-  constexpr int NIT = kKeysPerWave / 4;   // lane keys: 4 it + grp
-  constexpr int NKB = kKeysPerWave / 16;  // 16-key score blocks
-  constexpr int NKS = kKeysPerWave / 32;  // 32-key value steps
-  static_assert(kKeysPerWave % 32 == 0 && G <= 8, "whole value steps; a wave's partial fits its key buffer");
-  // per wave: one 16-key block of K (row-major, 16-byte granules xor-swizzled
-  // by the row), later the wave's partial o[G][D] in fp32
-  __shared__ __attribute__((aligned(16))) uint16_t s_k[kWavesPerUnit][16 * D];
-  __shared__ float s_m[kWavesPerUnit][G];
-  __shared__ float s_l[kWavesPerUnit][G];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[G * D];  // the G query heads
+    const int2* __restrict__ runs, const int* __restrict__ n_runs, int Hkv, int64_t max_len,
+    int max_runs, float sscale, float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  constexpr int LD = D / 16;  // dims per lane in the token-major loads
+  constexpr int NDW = LD / 2;
+  constexpr int KS = D / 32;  // MFMA k-steps over the head dimension
+  constexpr int NG = D / 8;   // 16-byte granules per key row
+  static_assert(G <= 8, "heads 4 grp + r of the value product cover at most 16");
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][16 * D];  // per-wave K tile
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[G * D];
+  __shared__ float s_o[2][G * D];      // half 1's O at a unit's end (two units alternate)
+  __shared__ float s_ml[2][2][2][G];   // [unit parity][half][m, l][head]
+  // the run's unit partials, merged at its end: head h, unit i of the run at
+  // s_part[(h * kDecodeRun + i) * D ...], (m, l) at s_pml[(h * kDecodeRun + i) * 2 ...]
+  __shared__ __attribute__((aligned(16))) float s_part[G * kDecodeRun * D];
+  __shared__ float s_pml[G * kDecodeRun * 2];
 
-  const int g = blockIdx.x;   // kv heads of one key block are dispatched together
-  // (request, unit) from a host-built list of real units, or the full grid
-  const int b = units ? units[blockIdx.y].x : int(blockIdx.z);
-  const int s = units ? units[blockIdx.y].y : int(blockIdx.y);
+  if (n_runs && int(blockIdx.x) >= *n_runs) return;
+  const int2 run = runs[blockIdx.x];
+  const int b = run.x;
+  const int u0 = run.y;
+  const int g = blockIdx.y;
   const DecodeSeq sq = seqs[b];
   const int64_t L = sq.kv_len;
   if (L < 1 || L > max_len) return;  // the combine kernel reports the request as NaN
-  const int64_t nsplit = (L + kSplit - 1) / kSplit;
-  if (s >= nsplit) return;
-
+  const int n_units = int((L + kSplit - 1) / kSplit);
+  if (u0 < 0 || u0 >= n_units) return;
+  const int nu = min(kDecodeRun, n_units - u0);
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int kh = int(wave_uniform(threadIdx.x >> 6));  // key half of every block (scalar: uniform loops)
   const int l16 = lane & 15;
   const int grp = lane >> 4;
-  const int Hq = Hkv * G;
-  const int64_t row_stride = int64_t(Hkv) * D;
-  const int64_t key_base = int64_t(s) * kSplit + w * kKeysPerWave;
+  const int nblk = int((L + KB - 1) / KB);
+  // blocks of this run for this half: half 1 has no key in a last block holding <= 32 keys
+  const int blk0 = u0 * kUnitBlocks;
+  const int blk_end = min((u0 + nu) * kUnitBlocks, nblk) - (kh == 1 && L - int64_t(nblk - 1) * KB <= 32 && (u0 + nu) * kUnitBlocks >= nblk ? 1 : 0);
 
-  // ---- loads.  Query: the G rows of this kv head, 16 bytes per thread.
-  const bool q_thread = threadIdx.x < G * D / 8;
-  uint32_t qv[4];
-  buf_ld_stream<4>(buf_rsrc(q + sq.q_row * q_stride + g * G * D, G * D * 2), threadIdx.x * 16, qv);
-  // Keys and values: lane (grp, l16) takes dims LD l16 .. + LD of keys
-  // key_base + 4 it + grp; the buffers end at the unit's last valid key.
-  const int64_t left = L - int64_t(s) * kSplit;
-  const uint32_t nv = uint32_t(left < kSplit ? left : kSplit);
+  const int64_t row_stride = int64_t(Hkv) * D;
   const uint32_t row_bytes = uint32_t(row_stride) * 2;
-  const int64_t unit_row = sq.kv_offset + int64_t(s) * kSplit;
-  const __amdgpu_buffer_rsrc_t krs = buf_rsrc(k_all + unit_row * row_stride + g * D, nv * row_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(v_all + unit_row * row_stride + g * D, nv * row_bytes);
-  const uint32_t lane_off = uint32_t(w * kKeysPerWave + grp) * row_bytes + uint32_t(l16) * LD * 2;
-  uint32_t kw[NIT][NDW], vw[NIT][NDW];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) buf_ld_stream<NDW>(krs, lane_off + uint32_t(4 * it) * row_bytes, kw[it]);
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) buf_ld_stream<NDW>(vrs, lane_off + uint32_t(4 * it) * row_bytes, vw[it]);
-  if (q_thread) *reinterpret_cast<uint4*>(s_q + threadIdx.x * 8) = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+  const uint16_t* kbase = k_all + sq.kv_offset * row_stride + g * D;
+  const uint16_t* vbase = v_all + sq.kv_offset * row_stride + g * D;
+  const uint32_t lane_off = uint32_t(grp) * row_bytes + uint32_t(l16) * LD * 2;
+
+  {
+    uint32_t qv[4];
+    buf_ld_stream<4>(buf_rsrc(q + sq.q_row * q_stride + g * G * D, G * D * 2), threadIdx.x * 16, qv);
+    if (threadIdx.x < G * D / 8) *reinterpret_cast<uint4*>(s_q + threadIdx.x * 8) = make_uint4(qv[0], qv[1], qv[2], qv[3]);
+  }
   __syncthreads();
 
-  // ---- S^T = K Q^T, one 16-key block kb at a time through the wave's LDS
-  // buffer.  Block row i holds wave key 16 kb + 4 (i & 3) + (i >> 2), so output
-  // register r of lane (head l16, grp) is the score of key 4 (4 kb + r) + grp:
-  // the keys of the lane's own value registers.
-  uint16_t* sk = s_k[w];
-  f32x4 sacc[NKB];
+  // lane's keys of block blk: 64 blk + 32 kh + 4 it + grp, it = 0..7, dims LD l16 .. + LD
+  uint32_t kw[8][NDW], vw[8][NDW], nkw[8][NDW], nvw[8][NDW];
+  auto load = [&](uint32_t (&kd)[8][NDW], uint32_t (&vd)[8][NDW], int blk) {
+    const int64_t first = int64_t(blk) * KB + 32 * kh;
+    const int64_t left = (blk < blk_end ? L : 0) - first;  // nothing is read past the run
+    const uint32_t nv = uint32_t(left <= 0 ? 0 : (left < 32 ? left : 32));
+    const __amdgpu_buffer_rsrc_t krs = buf_rsrc(wave_uniform(kbase + first * row_stride), wave_uniform(nv * row_bytes));
+    const __amdgpu_buffer_rsrc_t vrs = buf_rsrc(wave_uniform(vbase + first * row_stride), wave_uniform(nv * row_bytes));
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
+    for (int it = 0; it < 8; ++it) buf_ld_stream<NDW>(krs, lane_off + uint32_t(4 * it) * row_bytes, kd[it]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kr = 4 * j + grp;  // key row within the block
-      const uint32_t* src = kw[4 * kb + j];
-      if constexpr (NDW == 4) {
-        const int phys = l16 ^ (kr & (NG - 1));
-        *reinterpret_cast<uint4*>(sk + kr * D + phys * 8) = make_uint4(src[0], src[1], src[2], src[3]);
-      } else {
-        const int phys = (l16 >> 1) ^ (kr & (NG - 1));
-        *reinterpret_cast<uint2*>(sk + kr * D + phys * 8 + (l16 & 1) * 4) = make_uint2(src[0], src[1]);
+    for (int it = 0; it < 8; ++it) buf_ld_stream<NDW>(vrs, lane_off + uint32_t(4 * it) * row_bytes, vd[it]);
+  };
+
+  f32x4 oacc[LD];
+  float m_run, l_run;
+  auto reset = [&] {
+#pragma unroll
+    for (int e = 0; e < LD; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run = -INFINITY;
+    l_run = 0.f;
+  };
+  reset();
+  uint16_t* sk = s_k[kh];
+  const int rr = 4 * (l16 & 3) + (l16 >> 2);  // K tile row read as MFMA row l16
+
+  // one block: scores, online softmax (reference maximum moves when the block maximum
+  // exceeds it by more than 8) and value product of this wave's 32 keys
+  auto process = [&](const uint32_t (&kd)[8][NDW], const uint32_t (&vd)[8][NDW], int blk) {
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kr = 4 * j + grp;
+        const uint32_t* src = kd[4 * kb + j];
+        if constexpr (NDW == 4) {
+          const int phys = l16 ^ (kr & (NG - 1));
+          *reinterpret_cast<uint4*>(sk + kr * D + phys * 8) = make_uint4(src[0], src[1], src[2], src[3]);
+        } else {
+          const int phys = (l16 >> 1) ^ (kr & (NG - 1));
+          *reinterpret_cast<uint2*>(sk + kr * D + phys * 8 + (l16 & 1) * 4) = make_uint2(src[0], src[1]);
+        }
+      }
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int phys = (4 * ks + grp) ^ (rr & (NG - 1));
+        const uint4 a = *reinterpret_cast<const uint4*>(sk + rr * D + phys * 8);
+        const uint4 qq = l16 < G ? *reinterpret_cast<const uint4*>(s_q + l16 * D + 32 * ks + 8 * grp)
+                                 : make_uint4(0, 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qq), sacc[kb], 0, 0, 0);
       }
     }
-    const int rr = 4 * (l16 & 3) + (l16 >> 2);
-    sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bool last = blk == nblk - 1;
+    const int64_t key0 = int64_t(blk) * KB + 32 * kh + grp;
+    float p[8];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      // A operand: K[row rr][32 ks + 8 grp .. + 8]; B operand: Q[head l16][same dims] (0 past G)
-      const int phys = (4 * ks + grp) ^ (rr & (NG - 1));
-      const uint4 a = *reinterpret_cast<const uint4*>(sk + rr * D + phys * 8);
-      const uint4 qq = l16 < G ? *reinterpret_cast<const uint4*>(s_q + l16 * D + 32 * ks + 8 * grp)
-                               : make_uint4(0, 0, 0, 0);
-      sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qq), sacc[kb], 0, 0, 0);
-    }
-  }
-
-  // ---- softmax over the unit: lane holds head l16, keys key_base + 4 it + grp
-  float sc[NIT];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int it = 4 * kb + r;
-      const bool valid = key_base + 4 * it + grp < L;
-      const float v = valid ? sacc[kb][r] * qscale : -INFINITY;
-      sc[it] = v;
+    for (int j = 0; j < 8; ++j) {
+      float v = sacc[j >> 2][j & 3] * sscale;
+      if (last && key0 + 4 * j >= L) v = -INFINITY;
+      p[j] = v;
       mx = fmaxf(mx, v);
     }
-  mx = max_x32(max_x16(mx));
-  if (grp == 0 && l16 < G) s_m[w][l16] = mx;
-  __syncthreads();
-  const int hh = l16 < G ? l16 : 0;
-  float m = s_m[0][hh];
+    mx = max_x32(max_x16(mx));
+    const bool lift = mx > m_run + 8.0f;
+    const float m_new = lift ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
 #pragma unroll
-  for (int ww = 1; ww < kWavesPerUnit; ++ww) m = fmaxf(m, s_m[ww][hh]);
-  float p[NIT];
-  float ls = 0.f;
+    for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(p[j] - m_new);
+    float cs = p[0];
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    p[it] = l16 < G ? __builtin_amdgcn_exp2f(sc[it] - m) : 0.f;
-    ls += p[it];
-  }
-  ls = sum_x32(sum_x16(ls));
-  if (grp == 0 && l16 < G) s_l[w][l16] = ls;
-  // P as a bf16 high part plus a bf16 remainder (A operand: row head l16,
-  // k = it of the lane's key group)
-  uint4 ph[NKS], pl[NKS];
+    for (int j = 1; j < 8; ++j) cs += p[j];
+    const float tc = cs + __shfl_xor(cs, 32, 64);
+    const float rs = tc + __shfl_xor(tc, 16, 64);
+    l_run = __builtin_fmaf(l_run, alpha, rs);
+    // O's rows are heads 4 grp + r, each scaled by its own head's alpha; skipped, exactly,
+    // when every alpha of the wave is 1 (no reference maximum moved)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-  for (int kk = 0; kk < NKS; ++kk) {
-    uint32_t h4[4], l4[4];
+      for (int r = 0; r < 4; ++r) {
+        const float ar = __shfl(alpha, 4 * grp + r, 64);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float p0 = p[8 * kk + 2 * j], p1 = p[8 * kk + 2 * j + 1];
-      const uint16_t a = f2bf(p0), c = f2bf(p1);
-      h4[j] = uint32_t(a) | (uint32_t(c) << 16);
-      l4[j] = pack2bf(p0 - bf2f(a), p1 - bf2f(c));
+        for (int e = 0; e < LD; ++e) oacc[e][r] *= ar;
+      }
     }
-    ph[kk] = make_uint4(h4[0], h4[1], h4[2], h4[3]);
-    pl[kk] = make_uint4(l4[0], l4[1], l4[2], l4[3]);
-  }
-
-  // ---- O = P V, one MFMA block per lane dim e: B operand lane (col l16, grp)
-  // holds V[key 4 it + grp][dim LD l16 + e], it = 8 kk .. 8 kk + 7, regrouped
-  // from the token-major registers by byte permutes.  Lane (l16, grp) gets
-  // heads 4 grp + r of dim LD l16 + e; the wave's partial goes into its own
-  // (now free) key buffer.
-  float* so = reinterpret_cast<float*>(sk);
+    uint32_t h4[4], w4[4];
 #pragma unroll
-  for (int e = 0; e < LD; ++e) {
-    f32x4 oacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t hp = pack2bf(p[2 * jj], p[2 * jj + 1]);
+      h4[jj] = hp;
+      w4[jj] = pack2bf(p[2 * jj] - bf2f_lo(hp), p[2 * jj + 1] - bf2f_hi(hp));
+    }
+    const bf16x8 ph = as_bf16x8(make_uint4(h4[0], h4[1], h4[2], h4[3]));
+    const bf16x8 pl = as_bf16x8(make_uint4(w4[0], w4[1], w4[2], w4[3]));
 #pragma unroll
-    for (int kk = 0; kk < NKS; ++kk) {
+    for (int e = 0; e < LD; ++e) {
       uint32_t vt[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        vt[j] = __builtin_amdgcn_perm(vw[8 * kk + 2 * j + 1][e >> 1], vw[8 * kk + 2 * j][e >> 1],
-                                      (e & 1) ? 0x07060302u : 0x05040100u);
+      for (int jj = 0; jj < 4; ++jj)
+        vt[jj] = __builtin_amdgcn_perm(vd[2 * jj + 1][e >> 1], vd[2 * jj][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
       const bf16x8 vb = as_bf16x8(make_uint4(vt[0], vt[1], vt[2], vt[3]));
-      oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ph[kk]), vb, oacc, 0, 0, 0);
-      oacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pl[kk]), vb, oacc, 0, 0, 0);
+      oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[e], 0, 0, 0);
+      oacc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[e], 0, 0, 0);
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (4 * grp + r < G) so[(4 * grp + r) * D + LD * l16 + e] = oacc[r];
-  }
-  __syncthreads();
+  };
 
-  // ---- fixed-order sum over the waves; write the unit's partials
-  for (int i = threadIdx.x; i < G * D; i += kSplitThreads) {
-    const int h = i / D;
-    const int d = i % D;
-    float o = reinterpret_cast<const float*>(s_k[0])[h * D + d];
+  // end of unit i of the run: merge the halves (half 0 first) into the unit's partial in
+  // LDS, then reset.  Lane (l16, grp) holds O of heads 4 grp + r, dims LD l16 + e.  Half 1's
+  // state alternates between two buffers, so one barrier per unit suffices: half 1 writes
+  // buffer i & 1 again only after the next unit's barrier, which half 0 passes after reading it.
+  auto finish_unit = [&](int i) {
+    const int pb = i & 1;
+    if (grp == 0 && l16 < G) {
+      s_ml[pb][kh][0][l16] = m_run;
+      s_ml[pb][kh][1][l16] = l_run;
+    }
+    if (kh == 1) {
 #pragma unroll
-    for (int ww = 1; ww < kWavesPerUnit; ++ww) o += reinterpret_cast<const float*>(s_k[ww])[h * D + d];
-    const int64_t slot = (int64_t(b) * Hq + g * G + h) * max_splits + s;
-    ws_o[slot * D + d] = o;
-    if (d == 0) {
-      float mm = s_m[0][h], ll = s_l[0][h];
+      for (int r = 0; r < 4; ++r)
+        if (4 * grp + r < G)
 #pragma unroll
-      for (int ww = 1; ww < kWavesPerUnit; ++ww) {
-        mm = fmaxf(mm, s_m[ww][h]);
-        ll += s_l[ww][h];
+          for (int e = 0; e < LD; ++e) s_o[pb][(4 * grp + r) * D + LD * l16 + e] = oacc[e][r];
+    }
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * grp + r;
+        if (h < G) {
+          const float m0 = s_ml[pb][0][0][h], l0 = s_ml[pb][0][1][h];
+          const float m1 = s_ml[pb][1][0][h], l1 = s_ml[pb][1][1][h];
+          const float mm = fmaxf(m0, m1);
+          const float a0 = __builtin_amdgcn_exp2f(m0 - mm);
+          const float a1 = __builtin_amdgcn_exp2f(m1 - mm);
+          float ov[LD];
+#pragma unroll
+          for (int e = 0; e < LD; ++e) ov[e] = __builtin_fmaf(oacc[e][r], a0, s_o[pb][h * D + LD * l16 + e] * a1);
+          float* dst = s_part + (h * kDecodeRun + i) * D + LD * l16;
+#pragma unroll
+          for (int e = 0; e < LD; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(ov[e], ov[e + 1], ov[e + 2], ov[e + 3]);
+          if (l16 == 0) {
+            s_pml[(h * kDecodeRun + i) * 2 + 0] = mm;
+            s_pml[(h * kDecodeRun + i) * 2 + 1] = __builtin_fmaf(l0, a0, l1 * a1);
+          }
+        }
       }
-      ws_ml[slot * 2 + 0] = mm;
-      ws_ml[slot * 2 + 1] = ll;
+    }
+    reset();
+  };
+
+  // the run's units in order; within a unit its (at most 4) blocks, two register sets
+  // alternating so the next block is in flight while one is processed.  A full unit has an
+  // even number of blocks, so every unit starts in the first set and the last load of a unit
+  // already brings the next unit's first block.  Both waves finish every unit (a half with no
+  // block in the run's last unit finishes it with an empty state).
+  if (blk0 < blk_end) load(kw, vw, blk0);
+  for (int i = 0; i < nu; ++i) {
+    const int ub = blk0 + kUnitBlocks * i;
+    const int ue = min(ub + kUnitBlocks, blk_end);
+    for (int blk = ub; blk < ue; blk += 2) {
+      load(nkw, nvw, blk + 1);  // past the run's blocks this reads nothing
+      process(kw, vw, blk);
+      if (blk + 1 >= ue) break;
+      load(kw, vw, blk + 2);
+      process(nkw, nvw, blk + 1);
+    }
+    finish_unit(i);
+  }
+  // the run's record: its units merged in ascending order (thread x: head x / D, dim x % D)
+  __syncthreads();
+  const int Hq = Hkv * G;
+  const int r = u0 / kDecodeRun;
+  for (int x = threadIdx.x; x < G * D; x += NT) {
+    const int h = x / D, d = x % D;
+    const float* pml = s_pml + h * kDecodeRun * 2;
+    const float* po = s_part + h * kDecodeRun * D + d;
+    float M = -INFINITY;
+    for (int i = 0; i < nu; ++i) M = fmaxf(M, pml[2 * i]);
+    float Lsum = 0.f, O = 0.f;
+    for (int i = 0; i < nu; ++i) {
+      const float w = __builtin_amdgcn_exp2f(pml[2 * i] - M);
+      Lsum = __builtin_fmaf(w, pml[2 * i + 1], Lsum);
+      O = __builtin_fmaf(w, po[i * D], O);
+    }
+    const int64_t slot = (int64_t(b) * Hq + g * G + h) * max_runs + r;
+    ws_o[slot * D + d] = O;
+    if (d == 0) {
+      ws_ml[slot * 2 + 0] = M;
+      ws_ml[slot * 2 + 1] = Lsum;
     }
   }
+}
+
+// number of runs of a request with L keys
+__device__ __host__ inline int runs_of(int64_t L) {
+  const int64_t units = (L + kSplit - 1) / kSplit;
+  return int((units + kDecodeRun - 1) / kDecodeRun);
 }
 
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml,
-    const DecodeSeq* __restrict__ seqs, int Hq, int max_splits, int64_t max_len,
+    const DecodeSeq* __restrict__ seqs, int Hq, int max_runs, int64_t max_len,
     uint16_t* __restrict__ o, int64_t o_stride) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -248,15 +328,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
     *dst = 0x7FC0;  // NaN: the request's length is outside what the grid covered
     return;
   }
-  const int S = int((L + kSplit - 1) / kSplit);
-  const int64_t base = (int64_t(b) * Hq + h) * max_splits;
-  // (unrolled so several units' loads are in flight; the sums stay in
-  // ascending s)
+  const int S = runs_of(L);
+  const int64_t base = (int64_t(b) * Hq + h) * max_runs;
   float M = -INFINITY;
-#pragma unroll 8
+#pragma unroll 4
   for (int s = 0; s < S; ++s) M = fmaxf(M, ws_ml[(base + s) * 2]);
   float Lsum = 0.f, O = 0.f;
-#pragma unroll 8
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
     const float w = __builtin_amdgcn_exp2f(ws_ml[(base + s) * 2] - M);
     Lsum = __builtin_fmaf(w, ws_ml[(base + s) * 2 + 1], Lsum);
@@ -265,71 +343,183 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
   *dst = f2bf(O / Lsum);
 }
 
-// Packs the standalone entry point's offset / length arrays into DecodeSeq.
-__global__ void decode_pack_kernel(const int64_t* __restrict__ kv_offset,
-                                   const int32_t* __restrict__ kv_len, int B,
-                                   DecodeSeq* __restrict__ out) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < B) {
-    DecodeSeq sq;
-    sq.q_row = b;
-    sq.kv_offset = kv_offset[b];
-    sq.kv_len = kv_len[b];
-    sq.pad = 0;
-    out[b] = sq;
+// Exclusive prefix sum over a 1024-thread work-group; `total` receives the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_w, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_w[w] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = s_w[i];
+    before += i < w ? t : 0;
+    all += t;
+  }
+  __syncthreads();  // s_w is reused by the next scan
+  total = all;
+  return before + x - v;
+}
+
+// Standalone entry point's set-up, one 1024-thread work-group: packs the offset / length
+// arrays into DecodeSeq and lists the runs (request, first unit) with the most units first
+// (every full run in request order, then the last runs of 7, 6, .., 1 units, each in
+// request order; the order the block entry point's host list has).  A request whose length
+// is outside 1 .. max_len gets no run (the combine kernel writes NaN for it).
+__global__ __launch_bounds__(1024) void decode_prep_kernel(const int64_t* __restrict__ kv_offset,
+                                                           const int32_t* __restrict__ kv_len, int B,
+                                                           int64_t max_len, DecodeSeq* __restrict__ seqs,
+                                                           int2* __restrict__ runs, int* __restrict__ n_runs) {
+  constexpr int R = kDecodeRun;
+  __shared__ int s_w[16];
+  __shared__ int s_base[R + 1];  // next free position of each class: R full runs, k < R last runs of k units
+  auto units = [&](int b) -> int {
+    const int64_t L = kv_len[b];
+    return (L >= 1 && L <= max_len) ? int((L + kSplit - 1) / kSplit) : 0;
+  };
+  // pass 1: runs per class
+  for (int k = R; k >= 1; --k) {
+    int c = 0;
+    for (int b = threadIdx.x; b < B; b += 1024) {
+      const int U = units(b);
+      c += k == R ? U / R : int(U % R == k);
+    }
+    int tot;
+    block_exclusive_scan(c, s_w, tot);
+    if (threadIdx.x == 0) s_base[k] = tot;  // the class's count, turned into its base below
+  }
+  if (threadIdx.x == 0) {
+    int at = 0;
+    for (int k = R; k >= 1; --k) {
+      const int n = s_base[k];
+      s_base[k] = at;
+      at += n;
+    }
+    *n_runs = at;
+  }
+  __syncthreads();
+  // pass 2: positions, 1024 requests at a time in request order.  s_base[k] is read before
+  // the class's scan and advanced by thread 0 after it (the scan's barriers order the two).
+  for (int c = 0; c < B; c += 1024) {
+    const int b = c + int(threadIdx.x);
+    int U = 0;
+    if (b < B) {
+      DecodeSeq sq;
+      sq.q_row = b;
+      sq.kv_offset = kv_offset[b];
+      sq.kv_len = kv_len[b];
+      sq.pad = 0;
+      seqs[b] = sq;
+      U = units(b);
+    }
+    const int f = U / R, p = U % R;
+    for (int k = R; k >= 1; --k) {
+      const int v = k == R ? f : int(p == k);
+      const int bk = s_base[k];
+      int tot;
+      const int at = block_exclusive_scan(v, s_w, tot);
+      if (k == R) {
+        for (int i = 0; i < f; ++i) runs[bk + at + i] = make_int2(b, i * R);
+      } else if (v) {
+        runs[bk + at] = make_int2(b, f * R);
+      }
+      if (threadIdx.x == 0) s_base[k] = bk + tot;
+    }
   }
 }
 
 template <int D, int G>
-hipError_t launch_split(const uint16_t* q, int64_t q_stride, const uint16_t* k_all,
-                        const uint16_t* v_all, const DecodeSeq* seqs, const int2* units,
-                        int n_units, int B, int64_t max_len, int max_splits, int Hkv, float qscale,
-                        float* ws_o, float* ws_ml, hipStream_t s) {
-  const dim3 grid = units ? dim3(Hkv, n_units, 1) : dim3(Hkv, max_splits, B);
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), grid, dim3(kSplitThreads), 0, s, q, q_stride, k_all,
-                     v_all, seqs, units, Hkv, max_len, max_splits, qscale, ws_o, ws_ml);
+hipError_t launch_units(const uint16_t* q, int64_t q_stride, const uint16_t* k_all, const uint16_t* v_all,
+                        const DecodeSeq* seqs, const int2* runs, const int* n_runs, int grid_runs, int64_t max_len,
+                        int max_runs, int Hkv, float sscale, float* ws_o, float* ws_ml, hipStream_t s) {
+  if (grid_runs <= 0) return hipSuccess;
+  hipLaunchKernelGGL((decode_unit_kernel<D, G>), dim3(grid_runs, Hkv), dim3(NT), 0, s, q, q_stride, k_all, v_all,
+                     seqs, runs, n_runs, Hkv, max_len, max_runs, sscale, ws_o, ws_ml);
   return hipGetLastError();
 }
 
+struct WsParts {
+  float* o;
+  float* ml;
+  DecodeSeq* seqs;
+  int2* runs;
+  int* n_runs;
+};
+
 }  // namespace
 
-// Workspace: ws_o [B][Hq][S][D] fp32, ws_ml [B][Hq][S][2] fp32, then the
-// packed DecodeSeq array of the standalone entry point; 256-byte aligned parts.
+// Workspace: ws_o [B][Hq][R][D] fp32 and ws_ml [B][Hq][R][2] fp32 (R = runs of the
+// longest request), then for the standalone entry point the packed DecodeSeq array,
+// the run list (B R pairs at most) and its length; 256-byte aligned parts.
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t decode_workspace_bytes(int B, int64_t max_kv_len, int Hq, int D) {
-  const int64_t S = (max_kv_len + kSplit - 1) / kSplit;
-  const size_t slots = size_t(B) * Hq * S;
-  return align256(slots * D * 4) + align256(slots * 2 * 4) + align256(size_t(B) * sizeof(DecodeSeq));
+static int max_runs_of(int64_t max_kv_len) { return runs_of(max_kv_len); }
+
+static WsParts ws_parts(void* ws, int B, int64_t max_kv_len, int Hq, int D, size_t* total) {
+  const size_t R = size_t(max_runs_of(max_kv_len));
+  const size_t slots = size_t(B) * Hq * R;
+  char* p = static_cast<char*>(ws);
+  size_t off = 0;
+  WsParts w;
+  w.o = reinterpret_cast<float*>(p + off);
+  off += align256(slots * D * 4);
+  w.ml = reinterpret_cast<float*>(p + off);
+  off += align256(slots * 2 * 4);
+  w.seqs = reinterpret_cast<DecodeSeq*>(p + off);
+  off += align256(size_t(B) * sizeof(DecodeSeq));
+  w.runs = reinterpret_cast<int2*>(p + off);
+  off += align256(size_t(B) * R * sizeof(int2));
+  w.n_runs = reinterpret_cast<int*>(p + off);
+  off += 256;
+  if (total) *total = off;
+  return w;
 }
 
-hipError_t launch_attn_decode(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_all,
-                              const uint16_t* v_all, const DecodeSeq* d_seqs, const int2* d_units,
-                              int n_units, int B, int64_t max_kv_len, int Hq, int Hkv, int D,
-                              float scale, void* ws, uint16_t* o, int64_t o_row_stride,
-                              hipStream_t s) {
-  const int max_splits = int((max_kv_len + kSplit - 1) / kSplit);
-  const size_t slots = size_t(B) * Hq * max_splits;
-  float* ws_o = static_cast<float*>(ws);
-  float* ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(slots * D * 4));
-  const float qscale = scale * 1.4426950408889634f;  // scores in log2 units
+size_t decode_workspace_bytes(int B, int64_t max_kv_len, int Hq, int D) {
+  size_t total = 0;
+  ws_parts(nullptr, B, max_kv_len, Hq, D, &total);
+  return total;
+}
+
+static hipError_t run_decode(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_all, const uint16_t* v_all,
+                             const DecodeSeq* d_seqs, const int2* d_runs, const int* d_n_runs, int grid_runs, int B,
+                             int64_t max_kv_len, int Hq, int Hkv, int D, float scale, const WsParts& w, uint16_t* o,
+                             int64_t o_row_stride, hipStream_t s) {
+  const int max_runs = max_runs_of(max_kv_len);
+  const float qscale = scale * 1.4426950408889634f;  // scores in log2 units (as prefill)
   const int G = Hq / Hkv;
   hipError_t e = hipErrorInvalidValue;
-#define BI_DEC(DD, GG)                                                                          \
-  if (D == DD && G == GG)                                                                     \
-    e = launch_split<DD, GG>(q, q_row_stride, k_all, v_all, d_seqs, d_units, n_units, B, \
-                             max_kv_len, max_splits, Hkv, qscale, ws_o, ws_ml, s);
+#define BI_DEC(DD, GG)                                                                                 \
+  if (D == DD && G == GG)                                                                            \
+    e = launch_units<DD, GG>(q, q_row_stride, k_all, v_all, d_seqs, d_runs, d_n_runs, grid_runs, max_kv_len, \
+                             max_runs, Hkv, qscale, w.o, w.ml, s);
   BI_DEC(64, 1) BI_DEC(64, 2) BI_DEC(64, 4) BI_DEC(64, 8)
   BI_DEC(128, 1) BI_DEC(128, 2) BI_DEC(128, 4) BI_DEC(128, 8)
 #undef BI_DEC
   if (e != hipSuccess) return e;
   if (D == 64)
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(Hq, B), dim3(64), 0, s, ws_o, ws_ml, d_seqs,
-                       Hq, max_splits, max_kv_len, o, o_row_stride);
+    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(Hq, B), dim3(64), 0, s, w.o, w.ml, d_seqs, Hq, max_runs,
+                       max_kv_len, o, o_row_stride);
   else
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(Hq, B), dim3(128), 0, s, ws_o, ws_ml,
-                       d_seqs, Hq, max_splits, max_kv_len, o, o_row_stride);
+    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3(Hq, B), dim3(128), 0, s, w.o, w.ml, d_seqs, Hq, max_runs,
+                       max_kv_len, o, o_row_stride);
   return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_all,
+                              const uint16_t* v_all, const DecodeSeq* d_seqs, const int2* d_runs,
+                              int n_runs, int B, int64_t max_kv_len, int Hq, int Hkv, int D,
+                              float scale, void* ws, uint16_t* o, int64_t o_row_stride,
+                              hipStream_t s) {
+  if (!d_runs) return hipErrorInvalidValue;
+  const WsParts w = ws_parts(ws, B, max_kv_len, Hq, D, nullptr);
+  return run_decode(q, q_row_stride, k_all, v_all, d_seqs, d_runs, nullptr, n_runs, B, max_kv_len, Hq, Hkv, D,
+                    scale, w, o, o_row_stride, s);
 }
 
 hipError_t launch_attn_decode_arrays(const uint16_t* q, const uint16_t* k_all,
@@ -337,16 +527,15 @@ hipError_t launch_attn_decode_arrays(const uint16_t* q, const uint16_t* k_all,
                                      const int32_t* kv_len, int B, int64_t max_kv_len, int Hq,
                                      int Hkv, int D, float scale, void* ws, uint16_t* o,
                                      hipStream_t s) {
-  const int max_splits = int((max_kv_len + kSplit - 1) / kSplit);
-  const size_t slots = size_t(B) * Hq * max_splits;
-  DecodeSeq* seqs = reinterpret_cast<DecodeSeq*>(static_cast<char*>(ws) + align256(slots * D * 4) +
-                                                 align256(slots * 2 * 4));
-  hipLaunchKernelGGL(decode_pack_kernel, dim3((B + 255) / 256), dim3(256), 0, s, kv_offset, kv_len,
-                     B, seqs);
+  const WsParts w = ws_parts(ws, B, max_kv_len, Hq, D, nullptr);
+  hipLaunchKernelGGL(decode_prep_kernel, dim3(1), dim3(1024), 0, s, kv_offset, kv_len, B, max_kv_len, w.seqs,
+                     w.runs, w.n_runs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_attn_decode(q, int64_t(Hq) * D, k_all, v_all, seqs, nullptr, 0, B, max_kv_len,
-                            Hq, Hkv, D, scale, ws, o, int64_t(Hq) * D, s);
+  const int64_t grid = int64_t(B) * max_runs_of(max_kv_len);  // bound on the list's length
+  if (grid > (int64_t(1) << 24)) return hipErrorInvalidValue;  // grid x stays far below 2^32 threads
+  return run_decode(q, int64_t(Hq) * D, k_all, v_all, w.seqs, w.runs, w.n_runs, int(grid), B, max_kv_len, Hq, Hkv,
+                    D, scale, w, o, int64_t(Hq) * D, s);
 }
 
 }  // namespace bi

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
     L = kv_len[b];
   }
   const int lane = threadIdx.x & 63;
-  const int kh = threadIdx.x >> 6;  // key half of every block
+  const int kh = int(wave_uniform(threadIdx.x >> 6));  // key half of every block (scalar: uniform loops)
   const int l16 = lane & 15;
   const int grp = lane >> 4;
   uint16_t* dst = o + qrow * o_stride + int64_t(g) * G * D;
@@ -222,12 +222,15 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
       const float tc = cs + __shfl_xor(cs, 32, 64);      // c0 + c2, c1 + c3
       const float rs = tc + __shfl_xor(tc, 16, 64);      // (c0 + c2) + (c1 + c3)
       l_run = __builtin_fmaf(l_run, alpha, rs);
-      // O's rows are heads 4 grp + r: each takes its own head's alpha (held by lane 4 grp + r)
+      // O's rows are heads 4 grp + r: each takes its own head's alpha (held by lane 4 grp + r).
+      // Skipped, exactly, when every alpha of the wave is 1 (no reference maximum moved).
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * grp + r, 64);
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha, 4 * grp + r, 64);
 #pragma unroll
-        for (int e = 0; e < LD; ++e) oacc[e][r] *= ar;
+          for (int e = 0; e < LD; ++e) oacc[e][r] *= ar;
+        }
       }
       // ---- O += P V: A = P (row head l16, k-slots 8 grp + j = class grp), B = V (col dim
       // LD l16 + e, same keys from the lane's own token-major registers)

@@ -16,6 +16,9 @@ constexpr int kGemmBK = 64;
 
 // Decode attention: fixed key/value split size.
 constexpr int kKvSplit = 256;
+// split decode: units 8 r .. 8 r + 7 of a request form run r; a run's units are
+// merged first (ascending), then the runs (ascending)
+constexpr int kDecodeRun = 8;
 
 // Prefill attention: key block size (blocks are aligned to absolute position 0).
 constexpr int kPrefillKeyBlock = 64;
@@ -60,11 +63,11 @@ struct DecodeSeq {
   int32_t pad;
 };
 size_t decode_workspace_bytes(int B, int64_t max_kv_len, int Hq, int D);
-// d_units: optional device list of (request, unit) pairs to compute (n_units
-// of them); nullptr launches every (request, unit < max units) pair.
+// d_runs: device list of (request, first unit) pairs, one per run of up to
+// kDecodeRun units (n_runs of them, each run of each request exactly once).
 hipError_t launch_attn_decode(const uint16_t* q, int64_t q_row_stride, const uint16_t* k_all,
-                              const uint16_t* v_all, const DecodeSeq* d_seqs, const int2* d_units,
-                              int n_units, int B, int64_t max_kv_len, int Hq, int Hkv, int D,
+                              const uint16_t* v_all, const DecodeSeq* d_seqs, const int2* d_runs,
+                              int n_runs, int B, int64_t max_kv_len, int Hq, int Hkv, int D,
                               float scale, void* ws, uint16_t* o, int64_t o_row_stride,
                               hipStream_t s);
 // Variant for the standalone entry point: separate offset / length arrays.

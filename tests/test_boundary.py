@@ -80,7 +80,9 @@ def test_attention_checks():
     assert L.bi_attn_prefill(P16, P16, P16b, P16c, 0, 4, 32, 8, 128, 0.0, NUL) == SHAPE
     assert L.bi_attn_prefill(MIS, P16, P16b, P16c, 0, 4, 32, 8, 128, sc, NUL) == ALIGN
     need = L.bi_attn_decode_workspace(4, 1000, 32, 128)
-    assert need >= 4 * 32 * 4 * 130 * 4
+    # one fp32 record (o[D], m, l) per (request, head, run of 8 units of 256 keys)
+    assert need >= 4 * 32 * 1 * 130 * 4
+    assert L.bi_attn_decode_workspace(4, 4097, 32, 128) >= 4 * 32 * 3 * 130 * 4
     args = lambda ws, nbytes, B=4, maxl=1000, D=128: (P16, P16b, P16c, P16, P16b, B, maxl, 32, 8, D, sc, ws,
                                                      nbytes, P16c, NUL)
     assert L.bi_attn_decode(*args(NUL, need)) == WS
@@ -112,8 +114,8 @@ def test_step_pack_layout():
     assert bi.lib().bi_step_pack(arr, len(SEQS), ctypes.c_void_p(buf.ctypes.data), nbytes - 1) == WS
     assert bi.lib().bi_step_pack(arr, len(SEQS), ctypes.c_void_p(buf.ctypes.data), nbytes) == OK
     hdr = buf[:40].view(np.int64)
-    # 3 sequences, 252 tokens, 1 prefill, 2 decodes with 701 and 1 keys: 3 + 1 units
-    assert list(hdr) == [3, n_tok, 1, 2, 4]
+    # 3 sequences, 252 tokens, 1 prefill, 2 decodes with 701 and 1 keys: 3 + 1 units, one run each
+    assert list(hdr) == [3, n_tok, 1, 2, 2]
     # prefill list at 256: {q_row, kv_base, q_start, q_len}
     pf = buf[256:256 + 24]
     assert pf[:16].view(np.int64).tolist() == [1, 1000] and pf[16:24].view(np.int32).tolist() == [250, 250]
@@ -129,8 +131,29 @@ def test_step_pack_layout():
     kvr = buf[kv_off:kv_off + 8 * n_tok].view(np.int64)
     assert kvr[0] == 700 and kvr[1] == 1250 and kvr[250] == 1499 and kvr[251] == 5000
     u_off = kv_off + ((8 * n_tok + 255) // 256) * 256
-    units = buf[u_off:u_off + 32].view(np.int32).reshape(4, 2)
-    assert units.tolist() == [[0, 0], [0, 1], [0, 2], [1, 0]]
+    runs = buf[u_off:u_off + 16].view(np.int32).reshape(2, 2)
+    assert runs.tolist() == [[0, 0], [1, 0]]
+
+
+def test_step_pack_run_list():
+    """Split decode's run list: (decode request, first unit) per run of 8 units of 256 keys, the
+    full runs first in request order, then the last runs by size (7 .. 1 units), each in request order."""
+    seqs = [dict(q_len=1, ctx_len=5000, kv_base=0),       # 5001 keys: 20 units, runs of 8, 8, 4
+            dict(q_len=7, ctx_len=0, kv_base=6000),       # a prefill
+            dict(q_len=1, ctx_len=100, kv_base=7000),     # 101 keys: 1 unit
+            dict(q_len=1, ctx_len=2100, kv_base=8000),    # 2101 keys: 9 units, runs of 8, 1
+            dict(q_len=1, ctx_len=1791, kv_base=12000)]   # 1792 keys: 7 units
+    arr = bi._seq_array(seqs)
+    nbytes = bi.lib().bi_step_meta_bytes(arr, len(seqs))
+    buf = np.zeros(nbytes, np.uint8)
+    assert bi.lib().bi_step_pack(arr, len(seqs), ctypes.c_void_p(buf.ctypes.data), nbytes) == OK
+    hdr = buf[:40].view(np.int64)
+    n_tok = 11
+    assert list(hdr) == [5, n_tok, 1, 4, 7]
+    off = 256 + 256 + 256 + ((4 * n_tok + 255) // 256) * 256 + ((8 * n_tok + 255) // 256) * 256
+    runs = buf[off:off + 7 * 8].view(np.int32).reshape(7, 2).tolist()
+    # decode indices: 0 (20 units), 1 (1 unit), 2 (9 units), 3 (7 units)
+    assert runs == [[0, 0], [0, 8], [2, 0], [3, 0], [0, 16], [1, 0], [2, 8]]
 
 
 def test_step_pack_rejects_bad_steps():

@@ -1,8 +1,10 @@
 """GPU parity and invariance of bi_attn_decode, bi_attn_prefill, bi_rope_kv,
 bi_add and bi_swiglu (through the C-ABI).
 
-Decode: fixed 256-key splits; every request's bits identical alone and in any
-batch, at split boundaries and for L = 1 (o = v exactly).  Prefill: chunking
+Decode: fixed 256-key units merged in runs of 8 (2048 keys), then across runs;
+every request's bits identical alone and in any batch, at unit and run
+boundaries and for L = 1 (o = v exactly); requests outside 1 .. max_kv_len
+give NaN without disturbing the others.  Prefill: chunking
 invariance (one pass vs chunks, chunks starting mid-tile), t = 0 gives v0.
 """
 import math
@@ -37,7 +39,7 @@ def run_decode(q, k, v, offs, lens, max_len, hq, hkv, d):
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (4, 4, 64), (16, 2, 128), (8, 4, 64)])
 def test_decode_parity_split_boundaries(hq, hkv, d):
     device()
-    lens = np.array([1, 2, 255, 256, 257, 511, 512, 513, 1000, 2049])
+    lens = np.array([1, 2, 255, 256, 257, 511, 512, 513, 1000, 2048, 2049, 2304, 4097])
     announce("decode parity", hq, hkv, d, list(lens))
     k, v, offs = packed_kv(lens, hkv, d, 4000 + d + hq)
     q = synth.normal_bf16(4002 + hq, (len(lens), hq * d))
@@ -71,6 +73,31 @@ def test_decode_batch_invariance():
                                 max_len + 256 * rep, hq, hkv, d))
             for j, b in enumerate(idx):
                 assert_bitwise(o[j], alone[b], f"decode request {b} in batch {B}")
+
+
+def test_decode_many_requests_and_bad_lengths():
+    """1500 requests (the standalone entry point lists their runs on the device, 1024 requests
+    at a time): lengths 0 and above max_kv_len give NaN rows, every other row equals the
+    request decoded alone."""
+    device()
+    hq, hkv, d = 4, 1, 64
+    B, max_len = 1500, 2600
+    lens = synth.uniform_ints(4300, B, 1, max_len)
+    bad = np.array([3, 700, 1024, 1499])
+    lens[bad[:2]] = 0
+    lens[bad[2:]] = max_len + 1
+    kv_lens = np.maximum(lens, 1)
+    k, v, offs = packed_kv(kv_lens, hkv, d, 4301)
+    q = dev(synth.normal_bf16(4303, (B, hq * d)))
+    announce("decode B=1500 with bad lengths")
+    o = run_decode(q, k, v, offs, lens, max_len, hq, hkv, d).float().cpu().numpy()
+    ob = bits(run_decode(q, k, v, offs, lens, max_len, hq, hkv, d))
+    assert np.isnan(o[bad]).all()
+    good = np.setdiff1d(np.arange(B), bad)
+    assert np.isfinite(o[good]).all()
+    for b in np.random.default_rng(4304).choice(good, 12, replace=False):
+        alone = bits(run_decode(q[b:b + 1], k, v, offs[b:b + 1], lens[b:b + 1], max_len, hq, hkv, d))[0]
+        assert_bitwise(ob[b], alone, f"request {b} (L={lens[b]}) alone vs B=1500")
 
 
 def test_decode_config4_full_batch():
