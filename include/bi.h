@@ -154,14 +154,17 @@ bi_status bi_attn_prefill(const bi_bf16* q, const bi_bf16* k_cache, const bi_bf1
  * One query per request b over its L_b cached keys (the newest at position
  * L_b - 1), split into fixed 256-key units (M-0002 `technical`: a fixed split
  * size, not a fixed number of splits).  Unit s covers keys [256 s,
- * min(256 s + 256, L_b)); its (max, sum, weighted values) go to the workspace
- * in fp32, and a second kernel merges the units of each request in
- * ascending s.
+ * min(256 s + 256, L_b)) and is reduced on its own; units 8 r .. 8 r + 7 form
+ * run r and are merged in ascending order (max, sum, weighted values in
+ * fp32, one record per run and head in the workspace), and a second kernel
+ * merges the runs of each request in ascending r.  The merge tree depends
+ * only on L_b.
  *   q [B, Hq * D] bf16; k_all, v_all [sum L, Hkv, D] bf16 packed;
  *   kv_offset [B] int64 device: first row of request b in k_all / v_all;
  *   kv_len [B] int32 device: L_b, 1 <= L_b <= max_kv_len (a request outside
  *   that range gets NaN output, as the device cannot return an error);
- *   B >= 1 and max_kv_len >= 1 are host values used only to size the grid;
+ *   B >= 1 and max_kv_len >= 1 are host values used only to size the grid
+ *   (B * ceil(max_kv_len / 2048) <= 2^24);
  *   D in {64, 128}; Hq / Hkv in {1, 2, 4, 8}; o [B, Hq * D] bf16.
  *   ws: device workspace of at least bi_attn_decode_workspace() bytes.       */
 size_t bi_attn_decode_workspace(int B, int64_t max_kv_len, int Hq, int D);
