@@ -323,6 +323,8 @@ bi_status bi_attn_decode(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* 
   if (Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
   if (!head_shape_ok(Hq, Hkv, D, 8)) return BI_ERR_UNSUPPORTED;
   if (!scale_ok(scale)) return BI_ERR_SHAPE;
+  const int64_t run_keys = int64_t(bi::kKvSplit) * bi::kDecodeRun;
+  if (int64_t(B) * ((max_kv_len + run_keys - 1) / run_keys) > (int64_t(1) << 24)) return BI_ERR_UNSUPPORTED;
   if (!ws) return BI_ERR_WORKSPACE;
   if (ws_bytes < bi::decode_workspace_bytes(B, max_kv_len, Hq, D)) return BI_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_all) || !aligned16(v_all) || !aligned16(o) || !aligned16(ws) ||

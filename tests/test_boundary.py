@@ -90,6 +90,7 @@ def test_attention_checks():
     assert L.bi_attn_decode(*args(P16, need, B=0)) == SHAPE
     assert L.bi_attn_decode(*args(P16, need, maxl=0)) == SHAPE
     assert L.bi_attn_decode(*args(P16, need, D=80)) == UNSUP
+    assert L.bi_attn_decode(*args(P16, need, B=65535, maxl=1 << 30)) == UNSUP  # 2^24 runs at most
     assert L.bi_attn_decode(NUL, P16b, P16c, P16, P16b, 4, 1000, 32, 8, 128, sc, P16, need, P16c, NUL) == NULL
 
 
