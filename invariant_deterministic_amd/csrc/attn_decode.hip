@@ -382,13 +382,18 @@ __global__ __launch_bounds__(1024) void decode_prep_kernel(const int64_t* __rest
     const int64_t L = kv_len[b];
     return (L >= 1 && L <= max_len) ? int((L + kSplit - 1) / kSplit) : 0;
   };
-  // pass 1: runs per class
+  // pass 1: runs per class; a thread's counts packed in 8-bit fields (classes 1 .. R - 1,
+  // at most 64 requests each per thread while B <= 65536) and one count of full runs
+  static_assert(R == 8, "class counts are packed for runs of 8 units");
+  uint64_t packed = 0;
+  int full = 0;
+  for (int b = threadIdx.x; b < B; b += 1024) {
+    const int U = units(b);
+    full += U / R;
+    if (U % R) packed += uint64_t(1) << (8 * (U % R));
+  }
   for (int k = R; k >= 1; --k) {
-    int c = 0;
-    for (int b = threadIdx.x; b < B; b += 1024) {
-      const int U = units(b);
-      c += k == R ? U / R : int(U % R == k);
-    }
+    const int c = k == R ? full : int((packed >> (8 * k)) & 0xFF);
     int tot;
     block_exclusive_scan(c, s_w, tot);
     if (threadIdx.x == 0) s_base[k] = tot;  // the class's count, turned into its base below
