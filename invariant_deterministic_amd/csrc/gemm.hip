@@ -34,6 +34,16 @@
 // A is the weight tile, operand B the activation tile, so each lane ends with
 // 4 consecutive output columns of one output row and stores them as one
 // 8-byte write.
+//
+// bf16 weights use a second schedule of the same tile and the same per-element
+// MFMA chain (so the same bits): the eight waves form two groups of four, one
+// wave of each group per SIMD, that take turns -- while one group issues the
+// 16 MFMAs of half a stage from registers, the other reads its next
+// half-stage's fragments from LDS -- separated by work-group barriers, group 1
+// one barrier behind group 0.  Both operand tiles go from global memory
+// straight into LDS (global_load_lds_dwordx4, no staging registers), a stage
+// ahead, each LDS stage a separate array so the compiler can tell the pending
+// loads from the reads.
 #include <type_traits>
 
 #include "bi_dev.h"
@@ -267,6 +277,160 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
 #undef BI_STORE_LDS
 }
 
+// s_waitcnt immediates (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr unsigned kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr unsigned kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+
+// A work-group barrier that orders the compiler's memory operations but is no memory
+// fence: the schedule below waits for LDS reads (lgkmcnt) and direct loads (vmcnt)
+// itself, exactly where it needs them, so later loads stay in flight across barriers.
+__device__ __forceinline__ void ping_pong_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// bf16 GEMM, ping-pong schedule (see the file comment).  Offsets into A and W are
+// 32-bit byte offsets (the caller checks M K 2 and N K 2 < 2^32).
+__global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ W,
+                                                        uint16_t* __restrict__ C, int M, int N, int K,
+                                                        int tiles_n, int n_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW1[TILE];
+
+  const int wg = blockIdx.x;
+  const int tile = (n_tiles % 8 == 0) ? (wg % 8) * (n_tiles / 8) + wg / 8 : wg;
+  const int tm = tile / tiles_n;
+  const int tn = tile % tiles_n;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = int(__builtin_amdgcn_readfirstlane(t >> 6));
+  const int gp = wave >> 2;           // wave group; wave w runs on SIMD w % 4
+  const int s4 = wave & 3;
+  const int wn = s4 & 1;              // 128 output columns
+  const int wm = (s4 >> 1) + 2 * gp;  // 64 output rows
+
+  // Direct loads: wave w fills 1 KB blocks 4w .. 4w + 3 (tile rows 32w .. 32w + 31) of
+  // each operand tile; lane l writes bytes 16 l of its block: tile row 8 b + l / 8,
+  // stored chunk l % 8, which holds logical chunk (l % 8) ^ ((row / 2) % 8) (the layout
+  // lds_off describes).  Rows past M (past N) are clamped: computed, never stored.
+  const int a_last = M - 1, w_last = N - 1;
+  uint32_t a_vo[4], w_vo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * wave + 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    a_vo[j] = uint32_t(min(tm * BM + row, a_last)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
+    w_vo[j] = uint32_t(min(tn * BN + row, w_last)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
+  }
+  auto issue_loads = [&](int kt, uint16_t* dA, uint16_t* dW) {
+    const char* Ab = reinterpret_cast<const char*>(A + kt * BK);
+    const char* Wb = reinterpret_cast<const char*>(W + kt * BK);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(Ab + a_vo[j], dA + (4 * wave + j) * 512, 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(Wb + w_vo[j], dW + (4 * wave + j) * 512, 16, 0, 0);
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+    for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[bn][bm][r] = 0.f;
+
+  // fragment rows base + (lane & 31), base a multiple of 32, share the swizzle key
+  // ((lane & 31) / 2) % 8: a fragment's LDS offset is (row base) * BK + a lane offset
+  const int fr = lane & 31, fc = lane >> 5;
+  const int fkey = (fr >> 1) & 7;
+  const int a_base = (wm * 64) * BK, w_base = (wn * 128) * BK;
+  bf16x8 wf[2][4], af[2][2];
+  auto read_frags = [&](const uint16_t* sA, const uint16_t* sW, int h) {  // k-substeps 2h, 2h + 1
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int lo = fr * BK + (((2 * (2 * h + k2) + fc) ^ fkey) << 3);
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm) af[k2][bm] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo + bm * 32 * BK);
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) wf[k2][bn] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo + bn * 32 * BK);
+    }
+  };
+  // 32-row blocks entirely past M are skipped (padding work only)
+  const int wave_row0 = tm * BM + wm * 64;
+  const int nbm = wave_row0 >= M ? 0 : (wave_row0 + 32 >= M ? 1 : 2);
+  auto mfmas = [&](auto nbm_c) {
+    constexpr int NBM = decltype(nbm_c)::value;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn)
+#pragma unroll
+        for (int bm = 0; bm < NBM; ++bm)
+          acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[k2][bn], af[k2][bm], acc[bn][bm], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Stage k lives in LDS buffer k % 2.  Iteration k (every wave; group 1 one barrier
+  // later): [issue stage k + 1's loads, read half 0 of stage k] | [MFMAs] | [read half 1,
+  // wait for this wave's stage k + 1 loads] | [MFMAs], each part ending at a barrier.
+  // Stage k + 1's buffer last held stage k - 1, whose last reader (group 1, third part of
+  // iteration k - 1) passed a barrier before group 0 starts iteration k; every wave's
+  // stage k + 1 loads are complete before the barrier after which group 0 reads them.
+  const int KT = K / BK;
+  auto run = [&](auto nbm_c) {
+    issue_loads(0, sA0, sW0);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    if (gp == 1) ping_pong_barrier();
+    auto iter = [&](int k, uint16_t* cA, uint16_t* cW, uint16_t* nA, uint16_t* nW) {
+      if (k + 1 < KT) issue_loads(k + 1, nA, nW);
+      read_frags(cA, cW, 0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      ping_pong_barrier();
+      mfmas(nbm_c);
+      ping_pong_barrier();
+      read_frags(cA, cW, 1);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      ping_pong_barrier();
+      mfmas(nbm_c);
+      ping_pong_barrier();
+    };
+    for (int k = 0; k < KT; k += 2) {
+      iter(k, sA0, sW0, sA1, sW1);
+      if (k + 1 < KT) iter(k + 1, sA1, sW1, sA0, sW0);
+    }
+    if (gp == 0) ping_pong_barrier();
+  };
+  if (nbm == 2) run(std::integral_constant<int, 2>{});
+  else if (nbm == 1) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
+
+  // epilogue as gemm_kernel: acc[bn][bm][r] is C[m][n] with m = tile row base + wm*64 +
+  // bm*32 + (lane & 31), n = tile col base + wn*128 + bn*32 + 8*(r/4) + 4*(lane/32) + (r%4)
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm) {
+    const int m = tm * BM + wm * 64 + bm * 32 + (lane & 31);
+    if (m >= M) continue;
+    uint16_t* crow = C + int64_t(m) * N;
+#pragma unroll
+    for (int bn = 0; bn < 4; ++bn) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = tn * BN + wn * 128 + bn * 32 + 8 * q + 4 * (lane >> 5);
+        if (n < N) {
+          uint2 v;
+          v.x = pack2bf(acc[bn][bm][4 * q + 0], acc[bn][bm][4 * q + 1]);
+          v.y = pack2bf(acc[bn][bm][4 * q + 2], acc[bn][bm][4 * q + 3]);
+          *reinterpret_cast<uint2*>(crow + n) = v;
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, uint16_t* C, int64_t M, int64_t N,
@@ -274,9 +438,14 @@ hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, uint16_t* C, int64_
   const int tiles_m = int((M + BM - 1) / BM);
   const int tiles_n = int((N + BN - 1) / BN);
   const int n_tiles = tiles_m * tiles_n;
-  hipLaunchKernelGGL(gemm_kernel<false>, dim3(n_tiles), dim3(NT), 0, s, A,
-                     static_cast<const void*>(W), static_cast<const uint16_t*>(nullptr), C, int(M),
-                     int(N), int(K), tiles_n, n_tiles);
+  if (M * K * 2 < (int64_t(1) << 32) && N * K * 2 < (int64_t(1) << 32)) {
+    hipLaunchKernelGGL(gemm_pp_kernel, dim3(n_tiles), dim3(NT), 0, s, A, W, C, int(M), int(N), int(K), tiles_n,
+                       n_tiles);
+  } else {  // operands of 4 GiB or more: the register-staged schedule (64-bit addressing)
+    hipLaunchKernelGGL(gemm_kernel<false>, dim3(n_tiles), dim3(NT), 0, s, A,
+                       static_cast<const void*>(W), static_cast<const uint16_t*>(nullptr), C, int(M),
+                       int(N), int(K), tiles_n, n_tiles);
+  }
   return hipGetLastError();
 }
 
