@@ -47,9 +47,11 @@
 //
 // Work-group = 8 waves = (kv head g, tile of P = 128 / G positions): wave w
 // takes query head g*G + w % G, key half (w / G) % 2 and the 32 positions
-// tile + 32 (w / 2G).  The waves share the K / V^T blocks in LDS
-// (double-buffered through registers; half the threads move K, the other
-// half move V and transpose it 2 or 4 keys at a time).  Tiles run longest
+// tile + 32 (w / 2G).  The waves share the K / V^T blocks in LDS (four
+// stages filled through registers; half the threads move K, the other half
+// move V and transpose it 2 or 4 keys at a time).  The two waves of a SIMD
+// alternate, one phase apart: a block's score and value MFMAs in one phase,
+// its softmax in the next (see the block loop).  Tiles run longest
 // first; when a chunk has more tiles than the GPU has compute units, the grid
 // is folded so that work-group x runs tile n - 1 - x and then tile x, which
 // evens out the causal triangle.  Which work-group runs a tile never changes
@@ -108,9 +110,10 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
   constexpr int HT = NTH / 2;         // threads moving K (first half) or V (second half)
   constexpr int KPT = KB * DCH / HT;  // K chunks / V keys per thread
   static_assert(KPT == 2 || KPT == 4 || KPT == 8, "value transpose handles 2, 4 or 8 keys per thread");
-  static_assert(G * R * BD * 16 * 64 <= 2 * 2 * KB * D / 2, "the half-merge fits the block buffers");
+  constexpr int NS = 4;               // LDS stages: block b in stage b % 4
+  static_assert(G * R * BD * 16 * 64 <= 2 * NS * KB * D / 2, "the half-merge fits the block buffers");
   // [0][stage] = K block, [1][stage] = V^T block; after a tile, the merge buffer
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[2][2][KB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[2][NS][KB * D];
   __shared__ float s_ml[G * R][2][QW];
 
   const PrefillSeq sq = seqs ? seqs[blockIdx.z] : single;
@@ -257,17 +260,32 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     float m_run = -INFINITY;
     float l_run = 0.f;
 
+    // Schedule: waves w and w + 4 share a SIMD; group w / 4 = 1 runs one phase (barrier)
+    // behind group 0.  Iteration b = [MFMA phase: S(b), then O += V(b - 1) P(b - 1), block
+    // b + 2 stored into LDS] | [VALU phase: softmax of S(b) (mask, reference maximum,
+    // alpha, O *= alpha, P), loads of block b + 3 issued], so while one wave of a SIMD
+    // issues MFMAs the other runs its softmax.  Each row's operations and their order are
+    // those of the plain loop (O: ..., + V(b-1) P(b-1), * alpha(b), + V(b) P(b), ...).
+    // Block b lives in stage b % 4: written in the MFMA phase of iteration b - 2, read until
+    // group 1's MFMA phase of iteration b + 1.
+    const int grp = w >> 2;
+    const int nb_w = wave_active ? wave_end_blk : 0;  // blocks whose scores this wave computes
     load_block(0);
     store_block(0);
+    if (n_blk > 1) {
+      load_block(1);
+      store_block(1);
+    }
+    if (n_blk > 2) load_block(2);
     __syncthreads();
-    for (int blk = 0; blk < n_blk; ++blk) {
-      const int cur = blk & 1;
-      load_block(blk + 1 < n_blk ? blk + 1 : blk);  // the last step reloads its own block (unused)
-      if (wave_active && blk < wave_end_blk) {
-        const uint16_t* cK = sKV[0][cur];
-        const uint16_t* cV = sKV[1][cur];
+    if (grp == 1) __syncthreads();
+    f32x16 s;
+    bf16x8 p_hi[2], p_lo[2];
+    for (int blk = 0; blk <= n_blk; ++blk) {
+      // ---- MFMA phase
+      if (blk < nb_w) {
         // S^T: keys 32 kh .. 32 kh + 31 of the block, queries of the wave
-        f32x16 s;
+        const uint16_t* cK = sKV[0][blk % NS];
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
@@ -275,6 +293,35 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
           const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cK + k_off<D>(32 * kh + l32, 2 * kk + hf));
           s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
         }
+      }
+      if (blk >= 1 && blk - 1 < nb_w) {
+        // O^T[d][q] += V^T[d][key] P^T[key][q] for block blk - 1, P = hi + lo in bf16.  MFMA
+        // k-slot e of lane half hf in instruction `half` is register 8 half + e of S^T: key
+        // 4 e + c of class c = 2 half + hf, V^T positions 32 kh + 8 c + e.  Order: hi(0),
+        // hi(1), lo(0), lo(1).
+        const uint16_t* cV = sKV[1][(blk - 1) % NS];
+#pragma unroll
+        for (int bd = 0; bd < BD; ++bd) {
+          const int d = 32 * bd + l32;
+          bf16x8 vf[2];
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int pos = 32 * kh + 8 * (2 * half + hf);
+            const uint2 lo = *reinterpret_cast<const uint2*>(cV + vt_off(d, pos));
+            const uint2 hi = *reinterpret_cast<const uint2*>(cV + vt_off(d, pos + 4));
+            vf[half] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+          }
+          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0], p_hi[0], acc_o[bd], 0, 0, 0);
+          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], p_hi[1], acc_o[bd], 0, 0, 0);
+          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0], p_lo[0], acc_o[bd], 0, 0, 0);
+          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], p_lo[1], acc_o[bd], 0, 0, 0);
+        }
+      }
+      if (blk + 2 < n_blk) store_block((blk + 2) % NS);
+      __syncthreads();
+      // ---- VALU phase
+      if (blk + 3 < n_blk) load_block(blk + 3);
+      if (blk < nb_w) {
         // lane holds query wpos + l32; register r the key of class 2 (r / 8) + hf, j = r % 8
         const bool diag = blk == wave_last_blk;
         const int qpos = wpos + l32;
@@ -315,13 +362,6 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc_o[bd][r] *= alpha;
         }
-        // the next block goes into the free stage here, overlapping the PV MFMAs
-        if (blk + 1 < n_blk) store_block(cur ^ 1);
-        // O^T[d][q] += V^T[d][key] P^T[key][q], P = hi + lo in bf16.  MFMA
-        // k-slot e of lane half hf in instruction `half` is register
-        // 8 half + e of S^T: key 4 e + c of class c = 2 half + hf, V^T
-        // positions 32 kh + 8 c + e.  Order: hi(0), hi(1), lo(0), lo(1).
-        bf16x8 p_hi[2], p_lo[2];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           uint32_t hw[4], lw[4];
@@ -336,26 +376,10 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
           p_hi[half] = as_bf16x8(make_uint4(hw[0], hw[1], hw[2], hw[3]));
           p_lo[half] = as_bf16x8(make_uint4(lw[0], lw[1], lw[2], lw[3]));
         }
-#pragma unroll
-        for (int bd = 0; bd < BD; ++bd) {
-          const int d = 32 * bd + l32;
-          bf16x8 vf[2];
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int pos = 32 * kh + 8 * (2 * half + hf);
-            const uint2 lo = *reinterpret_cast<const uint2*>(cV + vt_off(d, pos));
-            const uint2 hi = *reinterpret_cast<const uint2*>(cV + vt_off(d, pos + 4));
-            vf[half] = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-          }
-          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0], p_hi[0], acc_o[bd], 0, 0, 0);
-          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], p_hi[1], acc_o[bd], 0, 0, 0);
-          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[0], p_lo[0], acc_o[bd], 0, 0, 0);
-          acc_o[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[1], p_lo[1], acc_o[bd], 0, 0, 0);
-        }
       }
-      if (!(wave_active && blk < wave_end_blk) && blk + 1 < n_blk) store_block(cur ^ 1);  // idle waves
       __syncthreads();
     }
+    if (grp == 0) __syncthreads();
 
     // ---- merge the key halves in a fixed order (half 0, half 1) and store.
     // Lane holds query wpos + l32 and dims 32 bd + 8 (r / 4) + 4 hf + r % 4.
