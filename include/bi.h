@@ -108,6 +108,26 @@ bi_status bi_gemm(const bi_bf16* A, const bi_bf16* W, bi_bf16* C,
 bi_status bi_gemm_w4(const bi_bf16* A, const uint8_t* Wq, const bi_f16* Ws, bi_bf16* C,
                      int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* GEMMs with the block's elementwise step fused into their epilogue.  Each
+ * element's reduction is the GEMM's (same MFMA chain, same tile for every M),
+ * so the bits equal the GEMM followed by bi_add or bi_swiglu:
+ *   bi_gemm_residual:  C = bf16(R + bf16(A W^T)), R and C [M, N] bf16 (C may
+ *                      alias R); the residual connection of the block;
+ *   bi_gemm_swiglu:    act[m, j] = bf16(silu(g) u), g = bf16((A W^T)[m, j]),
+ *                      u = bf16((A W^T)[m, F + j]) for W [2F, K] (gate rows,
+ *                      then up rows); act [M, F] bf16, F % 128 == 0 (the
+ *                      tile pairs gate and up columns of the same outputs);
+ *   _w4 forms: W given as int4 codes and fp16 scales as for bi_gemm_w4.
+ * Other size rules as bi_gemm (for bi_gemm_swiglu with N = 2F).              */
+bi_status bi_gemm_residual(const bi_bf16* A, const bi_bf16* W, const bi_bf16* R, bi_bf16* C,
+                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
+bi_status bi_gemm_swiglu(const bi_bf16* A, const bi_bf16* W, bi_bf16* act, int64_t M, int64_t F,
+                         int64_t K, hipStream_t stream);
+bi_status bi_gemm_w4_residual(const bi_bf16* A, const uint8_t* Wq, const bi_f16* Ws, const bi_bf16* R,
+                              bi_bf16* C, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+bi_status bi_gemm_w4_swiglu(const bi_bf16* A, const uint8_t* Wq, const bi_f16* Ws, bi_bf16* act,
+                            int64_t M, int64_t F, int64_t K, hipStream_t stream);
+
 /* --------------------------------------------------------- elementwise steps
  * h[i] = bf16(x[i] + o[i]) for i < n (the residual connection).  n % 8 == 0.
  * h may alias x or o.                                                        */

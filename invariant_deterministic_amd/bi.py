@@ -75,6 +75,10 @@ _SIGNATURES = {
     "bi_rmsnorm": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_float, c_void_p]),
     "bi_gemm": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
     "bi_gemm_w4": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
+    "bi_gemm_residual": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
+    "bi_gemm_swiglu": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
+    "bi_gemm_w4_residual": (c_int, [c_void_p] * 5 + [c_int64, c_int64, c_int64, c_void_p]),
+    "bi_gemm_w4_swiglu": (c_int, [c_void_p] * 4 + [c_int64, c_int64, c_int64, c_void_p]),
     "bi_add": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_void_p]),
     "bi_swiglu": (c_int, [c_void_p, c_void_p, c_int64, c_int64, c_void_p]),
     "bi_rope_kv": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int,
@@ -200,6 +204,53 @@ def gemm_w4(A, Wq, Ws, out=None):
         raise ValueError("int4 weight shape mismatch")
     out = torch.empty((M, N), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
     _check(lib().bi_gemm_w4(_ptr(A), _ptr(Wq), _ptr(Ws), _ptr(out), M, N, K, _stream()), "bi_gemm_w4")
+    return out
+
+
+def gemm_residual(A, W, R, out=None):
+    """out = R + A W^T (bf16), the residual add fused into the GEMM's epilogue."""
+    _dev(A, BF16, "A"); _dev(W, BF16, "W"); _dev(R, BF16, "R")
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K or R.shape != (M, N):
+        raise ValueError("shape mismatch")
+    out = torch.empty((M, N), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_gemm_residual(_ptr(A), _ptr(W), _ptr(R), _ptr(out), M, N, K, _stream()), "bi_gemm_residual")
+    return out
+
+
+def gemm_swiglu(A, W, out=None):
+    """act = swiglu(A W_gate^T, A W_up^T) for W [2F, K] (gate rows, then up rows)."""
+    _dev(A, BF16, "A"); _dev(W, BF16, "W")
+    M, K = A.shape
+    F = W.shape[0] // 2
+    if W.shape[1] != K or W.shape[0] != 2 * F:
+        raise ValueError("shape mismatch")
+    out = torch.empty((M, F), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_gemm_swiglu(_ptr(A), _ptr(W), _ptr(out), M, F, K, _stream()), "bi_gemm_swiglu")
+    return out
+
+
+def gemm_w4_residual(A, Wq, Ws, R, out=None):
+    _dev(A, BF16, "A"); _dev(Wq, torch.uint8, "Wq"); _dev(Ws, HALF_BITS, "Ws"); _dev(R, BF16, "R")
+    M, K = A.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] * 2 != K or Ws.shape != (N, K // 32) or R.shape != (M, N):
+        raise ValueError("shape mismatch")
+    out = torch.empty((M, N), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_gemm_w4_residual(_ptr(A), _ptr(Wq), _ptr(Ws), _ptr(R), _ptr(out), M, N, K, _stream()),
+           "bi_gemm_w4_residual")
+    return out
+
+
+def gemm_w4_swiglu(A, Wq, Ws, out=None):
+    _dev(A, BF16, "A"); _dev(Wq, torch.uint8, "Wq"); _dev(Ws, HALF_BITS, "Ws")
+    M, K = A.shape
+    F = Wq.shape[0] // 2
+    if Wq.shape[1] * 2 != K or Ws.shape != (2 * F, K // 32) or Wq.shape[0] != 2 * F:
+        raise ValueError("shape mismatch")
+    out = torch.empty((M, F), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    _check(lib().bi_gemm_w4_swiglu(_ptr(A), _ptr(Wq), _ptr(Ws), _ptr(out), M, F, K, _stream()), "bi_gemm_w4_swiglu")
     return out
 
 

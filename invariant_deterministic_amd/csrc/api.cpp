@@ -150,6 +150,9 @@ bi_status check_weight(const bi_weight& w, int fmt) {
   return BI_OK;
 }
 
+// the gate/up GEMM carries SwiGLU in its epilogue when its tile can pair the columns
+bool ffn_fused(const bi_block_cfg& c) { return c.ffn % 128 == 0; }
+
 struct WsLayout {
   bi_block_ws_layout pub;
 };
@@ -172,12 +175,14 @@ WsLayout ws_layout(const bi_block_cfg& c, const StepSummary& s) {
   L.pub.qkv = take(M * qkv * 2);
   L.pub.q = take(M * qd * 2);
   L.pub.attn = take(M * qd * 2);
-  L.pub.o = take(M * H * 2);
+  // o and d go straight into the residual sums h and y (fused epilogues); gu only when the
+  // gate/up GEMM cannot carry SwiGLU
+  L.pub.o = none;
   L.pub.h = F ? take(M * H * 2) : none;
   L.pub.n2 = F ? take(M * H * 2) : none;
-  L.pub.gu = F ? take(M * 2 * F * 2) : none;
+  L.pub.gu = F && !ffn_fused(c) ? take(M * 2 * F * 2) : none;
   L.pub.act = F ? take(M * F * 2) : none;
-  L.pub.d = F ? take(M * H * 2) : none;
+  L.pub.d = none;
   L.pub.decode_partials =
       s.n_decode && c.decode_order == BI_DECODE_SPLIT
           ? take(bi::decode_workspace_bytes(s.n_decode, s.max_decode_len, c.n_q_heads, c.head_dim))
@@ -196,11 +201,13 @@ const T* at(const void* base, size_t off) {
 }
 
 hipError_t run_gemm(const bi_block_cfg& c, const bi_weight& w, const uint16_t* A, uint16_t* C,
-                    int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                    int64_t M, int64_t N, int64_t K, hipStream_t s, int epi = bi::kEpiPlain,
+                    const uint16_t* R = nullptr) {
   if (c.weight_format == BI_WEIGHTS_INT4_G32)
-    return bi::launch_gemm_w4(A, static_cast<const uint8_t*>(w.w), w.scale, C, M, N, K, s);
-  return bi::launch_gemm(A, static_cast<const uint16_t*>(w.w), C, M, N, K, s);
+    return bi::launch_gemm_w4_ex(static_cast<const uint8_t*>(w.w), w.scale, A, R, C, M, N, K, epi, s);
+  return bi::launch_gemm_ex(A, static_cast<const uint16_t*>(w.w), R, C, M, N, K, epi, s);
 }
+
 
 }  // namespace
 
@@ -252,6 +259,44 @@ bi_status bi_gemm_w4(const bi_bf16* A, const uint8_t* Wq, const bi_f16* Ws, bi_b
   if (st != BI_OK) return st;
   if ((reinterpret_cast<uintptr_t>(Ws) & 1u) != 0) return BI_ERR_ALIGN;
   return from_hip(bi::launch_gemm_w4(A, Wq, Ws, C, M, N, K, stream));
+}
+
+bi_status bi_gemm_residual(const bi_bf16* A, const bi_bf16* W, const bi_bf16* R, bi_bf16* C, int64_t M, int64_t N,
+                           int64_t K, hipStream_t stream) {
+  if (!R) return BI_ERR_NULL;
+  const bi_status st = check_gemm(A, W, C, M, N, K);
+  if (st != BI_OK) return st;
+  if (!aligned16(R)) return BI_ERR_ALIGN;
+  return from_hip(bi::launch_gemm_ex(A, W, R, C, M, N, K, bi::kEpiResid, stream));
+}
+
+bi_status bi_gemm_swiglu(const bi_bf16* A, const bi_bf16* W, bi_bf16* act, int64_t M, int64_t F, int64_t K,
+                         hipStream_t stream) {
+  if (F < 1) return BI_ERR_SHAPE;
+  const bi_status st = check_gemm(A, W, act, M, 2 * F, K);
+  if (st != BI_OK) return st;
+  if (F % 128) return BI_ERR_UNSUPPORTED;
+  return from_hip(bi::launch_gemm_ex(A, W, nullptr, act, M, F, K, bi::kEpiGated, stream));
+}
+
+bi_status bi_gemm_w4_residual(const bi_bf16* A, const uint8_t* Wq, const bi_f16* Ws, const bi_bf16* R, bi_bf16* C,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (!Ws || !R) return BI_ERR_NULL;
+  const bi_status st = check_gemm(A, Wq, C, M, N, K);
+  if (st != BI_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(Ws) & 1u) != 0 || !aligned16(R)) return BI_ERR_ALIGN;
+  return from_hip(bi::launch_gemm_w4_ex(Wq, Ws, A, R, C, M, N, K, bi::kEpiResid, stream));
+}
+
+bi_status bi_gemm_w4_swiglu(const bi_bf16* A, const uint8_t* Wq, const bi_f16* Ws, bi_bf16* act, int64_t M,
+                            int64_t F, int64_t K, hipStream_t stream) {
+  if (!Ws) return BI_ERR_NULL;
+  if (F < 1) return BI_ERR_SHAPE;
+  const bi_status st = check_gemm(A, Wq, act, M, 2 * F, K);
+  if (st != BI_OK) return st;
+  if (F % 128) return BI_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(Ws) & 1u) != 0) return BI_ERR_ALIGN;
+  return from_hip(bi::launch_gemm_w4_ex(Wq, Ws, A, nullptr, act, M, F, K, bi::kEpiGated, stream));
 }
 
 bi_status bi_add(const bi_bf16* x, const bi_bf16* o, bi_bf16* h, int64_t n, hipStream_t stream) {
@@ -583,7 +628,6 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
   uint16_t* qkv = at<uint16_t>(ws, L.pub.qkv);
   uint16_t* q = at<uint16_t>(ws, L.pub.q);
   uint16_t* attn = at<uint16_t>(ws, L.pub.attn);
-  uint16_t* o = at<uint16_t>(ws, L.pub.o);
   uint16_t* h = F ? at<uint16_t>(ws, L.pub.h) : y;
 
   hipError_t e;
@@ -621,18 +665,19 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
                                   at<void>(ws, L.pub.decode_partials), attn, int64_t(Hq) * D,
                                   stream));
   }
-  BI_TRY(run_gemm(c, w->o, attn, o, M, H, int64_t(Hq) * D, stream));
-  BI_TRY(bi::launch_add(x, o, h, M * H, stream));
+  BI_TRY(run_gemm(c, w->o, attn, h, M, H, int64_t(Hq) * D, stream, bi::kEpiResid, x));  // h = x + o
   if (F) {
     uint16_t* n2 = at<uint16_t>(ws, L.pub.n2);
-    uint16_t* gu = at<uint16_t>(ws, L.pub.gu);
     uint16_t* act = at<uint16_t>(ws, L.pub.act);
-    uint16_t* d = at<uint16_t>(ws, L.pub.d);
     BI_TRY(bi::launch_rmsnorm(h, w->gamma2, n2, M, H, c.eps, stream));
-    BI_TRY(run_gemm(c, w->gate_up, n2, gu, M, 2 * int64_t(F), H, stream));
-    BI_TRY(bi::launch_swiglu(gu, act, M, F, stream));
-    BI_TRY(run_gemm(c, w->down, act, d, M, H, F, stream));
-    BI_TRY(bi::launch_add(h, d, y, M * H, stream));
+    if (ffn_fused(c)) {
+      BI_TRY(run_gemm(c, w->gate_up, n2, act, M, F, H, stream, bi::kEpiGated));
+    } else {
+      uint16_t* gu = at<uint16_t>(ws, L.pub.gu);
+      BI_TRY(run_gemm(c, w->gate_up, n2, gu, M, 2 * int64_t(F), H, stream));
+      BI_TRY(bi::launch_swiglu(gu, act, M, F, stream));
+    }
+    BI_TRY(run_gemm(c, w->down, act, y, M, H, F, stream, bi::kEpiResid, h));  // y = h + d
   }
 #undef BI_TRY
   return BI_OK;

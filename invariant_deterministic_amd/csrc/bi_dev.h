@@ -57,6 +57,12 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
   return r;
 }
 
+// SwiGLU of one element from bf16 inputs (as floats): silu(g) * u, silu(g) = g / (1 + e^-g).
+// One definition for the standalone kernel and the fused GEMM epilogue, so both round alike.
+__device__ __forceinline__ float swiglu1(float g, float u) { return (g / (1.0f + __expf(-g))) * u; }
+// Residual add of one element from bf16 inputs (as floats): x + o.
+__device__ __forceinline__ float resid1(float x, float o) { return x + o; }
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Butterfly sum over `width` lanes (a power of two <= 64) that differ only in

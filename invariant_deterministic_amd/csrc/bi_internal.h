@@ -26,6 +26,13 @@ constexpr int kPrefillKeyBlock = 64;
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, uint16_t* y, int64_t rows,
                           int64_t hidden, float eps, hipStream_t s);
 
+// GEMM epilogues (see gemm.hip): plain C = A W^T; residual C = R + A W^T (R [M, N]); gated
+// C = swiglu(A W_gate^T, A W_up^T) with W = [gate; up] of 2N rows and N % 128 == 0
+enum : int { kEpiPlain = 0, kEpiResid = 1, kEpiGated = 2 };
+hipError_t launch_gemm_ex(const uint16_t* A, const uint16_t* W, const uint16_t* R, uint16_t* C, int64_t M,
+                          int64_t N, int64_t K, int epi, hipStream_t s);
+hipError_t launch_gemm_w4_ex(const uint8_t* Wq, const uint16_t* Ws, const uint16_t* A, const uint16_t* R,
+                             uint16_t* C, int64_t M, int64_t N, int64_t K, int epi, hipStream_t s);
 hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, uint16_t* C, int64_t M, int64_t N,
                        int64_t K, hipStream_t s);
 hipError_t launch_gemm_w4(const uint16_t* A, const uint8_t* Wq, const uint16_t* Ws, uint16_t* C,

@@ -18,7 +18,7 @@ __global__ __launch_bounds__(256) void add_kernel(const uint4* __restrict__ x,
     unpack8(x[i], a);
     unpack8(o[i], b);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a[e] += b[e];
+    for (int e = 0; e < 8; ++e) a[e] = resid1(a[e], b[e]);
     h[i] = pack8(a);
   }
 }
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint16_t* __restrict_
     unpack8(*reinterpret_cast<const uint4*>(gu + r * 2 * F + c * 8), g);
     unpack8(*reinterpret_cast<const uint4*>(gu + r * 2 * F + F + c * 8), u);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) g[e] = (g[e] / (1.0f + __expf(-g[e]))) * u[e];
+    for (int e = 0; e < 8; ++e) g[e] = swiglu1(g[e], u[e]);
     *reinterpret_cast<uint4*>(act + r * F + c * 8) = pack8(g);
   }
 }

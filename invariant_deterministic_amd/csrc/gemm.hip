@@ -86,10 +86,77 @@ __device__ __forceinline__ void dequant_group_to_lds(const uint4& rq, uint16_t r
   }
 }
 
-template <bool W4>
+// Epilogues.  kEpiPlain: C = bf16(acc).  kEpiResid: C = bf16(R + bf16(acc)), the residual
+// add of the block fused into its GEMM (same roundings as the GEMM then the add).
+// kEpiGated: C[m][j] = bf16(swiglu(bf16(gate acc), bf16(up acc))) for the gate/up GEMM with
+// W = [gate rows 0 .. F - 1; up rows F .. 2F - 1]: a column tile covers outputs
+// 128 tn .. 128 tn + 127 and holds, in the blocks 0, 1 of the wave owning tile rows
+// 128 wn .. 128 wn + 127, the gate columns 64 wn + 32 b + i and in its blocks 2, 3 the up
+// columns of the same outputs, so a lane has both inputs of each of its outputs.  Every
+// element's MFMA chain is the same as in the plain GEMM: the bits of the fused forms equal
+// the GEMM followed by the elementwise kernel.
+// W row behind tile row t of column tile tn (F: the gated GEMM's output width)
+template <int EPI>
+__device__ __forceinline__ int w_row(int tn, int t, int F) {
+  if constexpr (EPI == kEpiGated) return ((t >> 6) & 1) * F + tn * 128 + ((t >> 7) << 6) + (t & 63);
+  else return tn * BN + t;
+}
+
+// acc[bn][bm][r] is tile element (row wm*64 + bm*32 + (lane & 31), column wn*128 + bn*32 +
+// 8*(r/4) + 4*(lane/32) + r%4); C has N columns (the gated form: N = F outputs)
+template <int EPI>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], uint16_t* __restrict__ C,
+                                           const uint16_t* __restrict__ R, int M, int N, int tm, int tn,
+                                           int wm, int wn, int lane) {
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm) {
+    const int m = tm * BM + wm * 64 + bm * 32 + (lane & 31);
+    if (m >= M) continue;
+    uint16_t* crow = C + int64_t(m) * N;
+    if constexpr (EPI == kEpiGated) {
+#pragma unroll
+      for (int bn = 0; bn < 2; ++bn) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = tn * 128 + wn * 64 + bn * 32 + 8 * q + 4 * (lane >> 5);
+          const uint32_t g01 = pack2bf(acc[bn][bm][4 * q + 0], acc[bn][bm][4 * q + 1]);
+          const uint32_t g23 = pack2bf(acc[bn][bm][4 * q + 2], acc[bn][bm][4 * q + 3]);
+          const uint32_t u01 = pack2bf(acc[bn + 2][bm][4 * q + 0], acc[bn + 2][bm][4 * q + 1]);
+          const uint32_t u23 = pack2bf(acc[bn + 2][bm][4 * q + 2], acc[bn + 2][bm][4 * q + 3]);
+          uint2 v;
+          v.x = pack2bf(swiglu1(bf2f_lo(g01), bf2f_lo(u01)), swiglu1(bf2f_hi(g01), bf2f_hi(u01)));
+          v.y = pack2bf(swiglu1(bf2f_lo(g23), bf2f_lo(u23)), swiglu1(bf2f_hi(g23), bf2f_hi(u23)));
+          *reinterpret_cast<uint2*>(crow + j) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int bn = 0; bn < 4; ++bn) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = tn * BN + wn * 128 + bn * 32 + 8 * q + 4 * (lane >> 5);
+          if (n < N) {
+            uint2 v;
+            v.x = pack2bf(acc[bn][bm][4 * q + 0], acc[bn][bm][4 * q + 1]);
+            v.y = pack2bf(acc[bn][bm][4 * q + 2], acc[bn][bm][4 * q + 3]);
+            if constexpr (EPI == kEpiResid) {
+              const uint2 x = *reinterpret_cast<const uint2*>(R + int64_t(m) * N + n);
+              v.x = pack2bf(resid1(bf2f_lo(x.x), bf2f_lo(v.x)), resid1(bf2f_hi(x.x), bf2f_hi(v.x)));
+              v.y = pack2bf(resid1(bf2f_lo(x.y), bf2f_lo(v.y)), resid1(bf2f_hi(x.y), bf2f_hi(v.y)));
+            }
+            *reinterpret_cast<uint2*>(crow + n) = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool W4, int EPI>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict__ A,
                                                      const void* __restrict__ Wv,
                                                      const uint16_t* __restrict__ Ws,
+                                                     const uint16_t* __restrict__ R,
                                                      uint16_t* __restrict__ C, int M, int N, int K,
                                                      int tiles_n, int n_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];
@@ -113,16 +180,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
   // Rows past M (past N for W) are clamped: computed, never stored.
   const int ld_chunk = t & 7;
   const int ld_row = t >> 3;
-  const int a_last = M - 1, w_last = N - 1;
+  const int a_last = M - 1, w_last = (EPI == kEpiGated ? 2 * N : N) - 1;
   const uint16_t* a_base = A + ld_chunk * 8;
   int a_r0 = min(tm * BM + ld_row, a_last), a_r1 = min(tm * BM + ld_row + 64, a_last);
   int a_r2 = min(tm * BM + ld_row + 128, a_last), a_r3 = min(tm * BM + ld_row + 192, a_last);
   const uint16_t* w_base = static_cast<const uint16_t*>(Wv) + ld_chunk * 8;
-  int w_r0 = min(tn * BN + ld_row, w_last), w_r1 = min(tn * BN + ld_row + 64, w_last);
-  int w_r2 = min(tn * BN + ld_row + 128, w_last), w_r3 = min(tn * BN + ld_row + 192, w_last);
+  int w_r0 = min(w_row<EPI>(tn, ld_row, N), w_last), w_r1 = min(w_row<EPI>(tn, ld_row + 64, N), w_last);
+  int w_r2 = min(w_row<EPI>(tn, ld_row + 128, N), w_last), w_r3 = min(w_row<EPI>(tn, ld_row + 192, N), w_last);
   const int q_row = t >> 1;  // int4: 256 rows x 2 groups of 32
   const int q_half = t & 1;
-  const int q_r = min(tn * BN + q_row, w_last);
+  const int q_r = min(w_row<EPI>(tn, q_row, N), w_last);
   const uint8_t* q_src = static_cast<const uint8_t*>(Wv) + int64_t(q_r) * (K / 2) + q_half * 16;
   const uint16_t* s_src = Ws + int64_t(q_r) * (K / 32) + q_half;
 
@@ -251,28 +318,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
   else if (nbm == 1) run(std::integral_constant<int, 1>{});
   else run(std::integral_constant<int, 0>{});
 
-  // ---- epilogue: acc[bn][bm][r] is C[m][n] with
-  //   m = tile row base + wm*64 + bm*32 + (lane & 31)
-  //   n = tile col base + wn*128 + bn*32 + 8*(r/4) + 4*(lane/32) + (r%4)
-#pragma unroll
-  for (int bm = 0; bm < 2; ++bm) {
-    const int m = tm * BM + wm * 64 + bm * 32 + (lane & 31);
-    if (m >= M) continue;
-    uint16_t* crow = C + int64_t(m) * N;
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = tn * BN + wn * 128 + bn * 32 + 8 * q + 4 * (lane >> 5);
-        if (n < N) {
-          uint2 v;
-          v.x = pack2bf(acc[bn][bm][4 * q + 0], acc[bn][bm][4 * q + 1]);
-          v.y = pack2bf(acc[bn][bm][4 * q + 2], acc[bn][bm][4 * q + 3]);
-          *reinterpret_cast<uint2*>(crow + n) = v;
-        }
-      }
-    }
-  }
+  store_tile<EPI>(acc, C, R, M, N, tm, tn, wm, wn, lane);
 #undef BI_LOAD_GLOBAL
 #undef BI_STORE_LDS
 }
@@ -288,8 +334,10 @@ __device__ __forceinline__ void ping_pong_barrier() { asm volatile("s_barrier" :
 
 // bf16 GEMM, ping-pong schedule (see the file comment).  Offsets into A and W are
 // 32-bit byte offsets (the caller checks M K 2 and N K 2 < 2^32).
+template <int EPI>
 __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ W,
+                                                        const uint16_t* __restrict__ R,
                                                         uint16_t* __restrict__ C, int M, int N, int K,
                                                         int tiles_n, int n_tiles) {
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[TILE];
@@ -314,14 +362,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
   // each operand tile; lane l writes bytes 16 l of its block: tile row 8 b + l / 8,
   // stored chunk l % 8, which holds logical chunk (l % 8) ^ ((row / 2) % 8) (the layout
   // lds_off describes).  Rows past M (past N) are clamped: computed, never stored.
-  const int a_last = M - 1, w_last = N - 1;
+  const int a_last = M - 1, w_last = (EPI == kEpiGated ? 2 * N : N) - 1;
   uint32_t a_vo[4], w_vo[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 32 * wave + 8 * j + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     a_vo[j] = uint32_t(min(tm * BM + row, a_last)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
-    w_vo[j] = uint32_t(min(tn * BN + row, w_last)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
+    w_vo[j] = uint32_t(min(w_row<EPI>(tn, row, N), w_last)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
   }
   auto issue_loads = [&](int kt, uint16_t* dA, uint16_t* dW) {
     const char* Ab = reinterpret_cast<const char*>(A + kt * BK);
@@ -408,55 +456,61 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
   else if (nbm == 1) run(std::integral_constant<int, 1>{});
   else run(std::integral_constant<int, 0>{});
 
-  // epilogue as gemm_kernel: acc[bn][bm][r] is C[m][n] with m = tile row base + wm*64 +
-  // bm*32 + (lane & 31), n = tile col base + wn*128 + bn*32 + 8*(r/4) + 4*(lane/32) + (r%4)
-#pragma unroll
-  for (int bm = 0; bm < 2; ++bm) {
-    const int m = tm * BM + wm * 64 + bm * 32 + (lane & 31);
-    if (m >= M) continue;
-    uint16_t* crow = C + int64_t(m) * N;
-#pragma unroll
-    for (int bn = 0; bn < 4; ++bn) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = tn * BN + wn * 128 + bn * 32 + 8 * q + 4 * (lane >> 5);
-        if (n < N) {
-          uint2 v;
-          v.x = pack2bf(acc[bn][bm][4 * q + 0], acc[bn][bm][4 * q + 1]);
-          v.y = pack2bf(acc[bn][bm][4 * q + 2], acc[bn][bm][4 * q + 3]);
-          *reinterpret_cast<uint2*>(crow + n) = v;
-        }
-      }
-    }
-  }
+  store_tile<EPI>(acc, C, R, M, N, tm, tn, wm, wn, lane);
 }
 
 }  // namespace
 
+// epi: kEpiPlain / kEpiResid (R [M, N]) / kEpiGated (N = F outputs, W [2F, K], F % 128 == 0)
+hipError_t launch_gemm_ex(const uint16_t* A, const uint16_t* W, const uint16_t* R, uint16_t* C, int64_t M,
+                          int64_t N, int64_t K, int epi, hipStream_t s) {
+  const int tiles_m = int((M + BM - 1) / BM);
+  const int tiles_n = epi == kEpiGated ? int(N / 128) : int((N + BN - 1) / BN);
+  const int n_tiles = tiles_m * tiles_n;
+  const int64_t w_rows = epi == kEpiGated ? 2 * N : N;
+  const bool pp = M * K * 2 < (int64_t(1) << 32) && w_rows * K * 2 < (int64_t(1) << 32);
+  const void* Wv = static_cast<const void*>(W);
+  const uint16_t* none = nullptr;
+#define BI_GEMM(E)                                                                                                   \
+  if (epi == E) {                                                                                                    \
+    if (pp)                                                                                                          \
+      hipLaunchKernelGGL(gemm_pp_kernel<E>, dim3(n_tiles), dim3(NT), 0, s, A, W, R, C, int(M), int(N), int(K),      \
+                         tiles_n, n_tiles);                                                                          \
+    else /* operands of 4 GiB or more: the register-staged schedule (64-bit addressing) */                         \
+      hipLaunchKernelGGL((gemm_kernel<false, E>), dim3(n_tiles), dim3(NT), 0, s, A, Wv, none, R, C, int(M), int(N), \
+                         int(K), tiles_n, n_tiles);                                                                  \
+    return hipGetLastError();                                                                                        \
+  }
+  BI_GEMM(kEpiPlain) BI_GEMM(kEpiResid) BI_GEMM(kEpiGated)
+#undef BI_GEMM
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_w4_ex(const uint8_t* Wq, const uint16_t* Ws, const uint16_t* A, const uint16_t* R,
+                             uint16_t* C, int64_t M, int64_t N, int64_t K, int epi, hipStream_t s) {
+  const int tiles_m = int((M + BM - 1) / BM);
+  const int tiles_n = epi == kEpiGated ? int(N / 128) : int((N + BN - 1) / BN);
+  const int n_tiles = tiles_m * tiles_n;
+  const void* Wv = static_cast<const void*>(Wq);
+#define BI_GEMM(E)                                                                                                 \
+  if (epi == E) {                                                                                                  \
+    hipLaunchKernelGGL((gemm_kernel<true, E>), dim3(n_tiles), dim3(NT), 0, s, A, Wv, Ws, R, C, int(M), int(N),    \
+                       int(K), tiles_n, n_tiles);                                                                  \
+    return hipGetLastError();                                                                                      \
+  }
+  BI_GEMM(kEpiPlain) BI_GEMM(kEpiResid) BI_GEMM(kEpiGated)
+#undef BI_GEMM
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(const uint16_t* A, const uint16_t* W, uint16_t* C, int64_t M, int64_t N,
                        int64_t K, hipStream_t s) {
-  const int tiles_m = int((M + BM - 1) / BM);
-  const int tiles_n = int((N + BN - 1) / BN);
-  const int n_tiles = tiles_m * tiles_n;
-  if (M * K * 2 < (int64_t(1) << 32) && N * K * 2 < (int64_t(1) << 32)) {
-    hipLaunchKernelGGL(gemm_pp_kernel, dim3(n_tiles), dim3(NT), 0, s, A, W, C, int(M), int(N), int(K), tiles_n,
-                       n_tiles);
-  } else {  // operands of 4 GiB or more: the register-staged schedule (64-bit addressing)
-    hipLaunchKernelGGL(gemm_kernel<false>, dim3(n_tiles), dim3(NT), 0, s, A,
-                       static_cast<const void*>(W), static_cast<const uint16_t*>(nullptr), C, int(M),
-                       int(N), int(K), tiles_n, n_tiles);
-  }
-  return hipGetLastError();
+  return launch_gemm_ex(A, W, nullptr, C, M, N, K, kEpiPlain, s);
 }
 
 hipError_t launch_gemm_w4(const uint16_t* A, const uint8_t* Wq, const uint16_t* Ws, uint16_t* C,
                           int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  const int tiles_m = int((M + BM - 1) / BM);
-  const int tiles_n = int((N + BN - 1) / BN);
-  const int n_tiles = tiles_m * tiles_n;
-  hipLaunchKernelGGL(gemm_kernel<true>, dim3(n_tiles), dim3(NT), 0, s, A,
-                     static_cast<const void*>(Wq), Ws, C, int(M), int(N), int(K), tiles_n, n_tiles);
-  return hipGetLastError();
+  return launch_gemm_w4_ex(Wq, Ws, A, nullptr, C, M, N, K, kEpiPlain, s);
 }
 
 }  // namespace bi

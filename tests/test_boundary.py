@@ -171,9 +171,16 @@ def test_block_workspace_layout():
     cfg = bi.BlockConfig(2560, 32, 8, 128, 9728, 1e-6, 1e6)
     lay = bi.block_workspace(cfg, SEQS)
     M = 252
-    offs = [lay.n1, lay.qkv, lay.q, lay.attn, lay.o, lay.h, lay.n2, lay.gu, lay.act, lay.d, lay.decode_partials]
+    none = ctypes.c_size_t(-1).value
+    # o and d are fused into the residual sums and, with F % 128 == 0, gate/up into SwiGLU:
+    # those stages are not materialised
+    assert lay.o == none and lay.d == none and lay.gu == none
+    offs = [lay.n1, lay.qkv, lay.q, lay.attn, lay.h, lay.n2, lay.act, lay.decode_partials]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
-    assert lay.qkv - lay.n1 >= M * 2560 * 2 and lay.act - lay.gu >= M * 2 * 9728 * 2
+    assert lay.qkv - lay.n1 >= M * 2560 * 2 and lay.decode_partials - lay.act >= M * 9728 * 2
+    # an FFN width the paired tile cannot cover keeps the gate/up stage
+    odd = bi.block_workspace(bi.BlockConfig(2560, 32, 8, 128, 9664, 1e-6, 1e6), SEQS)
+    assert odd.gu != none and odd.act - odd.gu >= M * 2 * 9664 * 2
     assert lay.total >= lay.decode_partials + bi.attn_decode_workspace(2, 701, 32, 128)
     nf = bi.block_workspace(bi.BlockConfig(256, 4, 4, 64, 0), [dict(q_len=128, ctx_len=0, kv_base=0)])
     assert nf.h == ctypes.c_size_t(-1).value and nf.decode_partials == ctypes.c_size_t(-1).value

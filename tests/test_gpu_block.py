@@ -62,10 +62,31 @@ def make_block(cfg, w):
 
 def stages(ws, lay, cfg, M):
     H, hq, hkv, d, F = (cfg[k] for k in ("hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn"))
-    widths = dict(n1=H, qkv=(hq + 2 * hkv) * d, q=hq * d, attn=hq * d, o=H)
+    widths = dict(n1=H, qkv=(hq + 2 * hkv) * d, q=hq * d, attn=hq * d)
     if F:
-        widths.update(h=H, n2=H, gu=2 * F, act=F, d=H)
+        # o and d live only inside the fused residual GEMMs, gate/up inside the SwiGLU GEMM
+        widths.update(h=H, n2=H, act=F)
     return {k: bits(bi.stage(ws, lay, k, M, wd)) for k, wd in widths.items()}
+
+
+def check_fused_stages(x, st, y, gemm, wdev, wref, F, tag=""):
+    """The O, gate/up and down projections run fused with their elementwise steps (residual
+    add, SwiGLU), so their GEMM outputs are never stored.  Rebuild each with the library's
+    unfused GEMM on the same rows (a row's GEMM output does not depend on the other rows),
+    check it against the oracle fed the GPU's previous stage, check the step after it against
+    the oracle on those bits, and check the fused stage bitwise against the unfused one."""
+    o = bits(gemm(dev(st["attn"]), wdev["w_o"]))
+    assert_within_tolerance(o, oracle.gemm(st["attn"], wref["w_o"]), "o" + tag)
+    assert_bitwise(st["h"], oracle.residual_add(x, o), "h = x + o" + tag)
+    assert_within_tolerance(st["n2"], oracle.rmsnorm(st["h"], wref["gamma2"], 1e-6), "n2" + tag)
+    gu = gemm(dev(st["n2"]), wdev["w_gate_up"])
+    gub = bits(gu)
+    assert_within_tolerance(gub, oracle.gemm(st["n2"], wref["w_gate_up"]), "gate/up" + tag)
+    assert_within_tolerance(st["act"], oracle.swiglu(gub[:, :F], gub[:, F:]), "swiglu" + tag)
+    assert_bitwise(st["act"], bits(bi.swiglu(gu)), "fused gate/up + swiglu vs unfused" + tag)
+    d = bits(gemm(dev(st["act"]), wdev["w_down"]))
+    assert_within_tolerance(d, oracle.gemm(st["act"], wref["w_down"]), "down" + tag)
+    assert_bitwise(y, oracle.residual_add(st["h"], d), "y = h + down" + tag)
 
 
 # ------------------------------------------------------------- tiny block
@@ -109,8 +130,11 @@ def test_tiny_block_invariance_and_parity():
                                            q[j * T:(j + 1) * T, 8:], np.arange(T), 1 / 8.0).reshape(T, -1)
                           for j in range(len(order))])
     assert_within_tolerance(st["attn"], att, "stage attention")
-    assert_within_tolerance(st["o"], oracle.gemm(st["attn"], w["w_o"]), "stage o")
-    assert_bitwise(yb, oracle.residual_add(x_all, st["o"]), "stage residual")
+    # the O projection is fused with the residual add: rebuild o with the unfused GEMM, check
+    # it against the oracle and the fused output bitwise against the oracle's add of those bits
+    o = bits(bi.gemm(dev(st["attn"]), dev(w["w_o"])))
+    assert_within_tolerance(o, oracle.gemm(st["attn"], w["w_o"]), "stage o")
+    assert_bitwise(yb, oracle.residual_add(x_all, o), "stage o + residual")
 
 
 # ------------------------------------------------------ dense block (4000)
@@ -153,13 +177,8 @@ def test_dense_block_parity_stagewise(dense_block):
     assert_bitwise(vpb[s0:s0 + c], qkv[:, 40:], "v in cache")
     att = oracle.attention(st["q"].reshape(c, 32, 128), kpb[:s0 + c], vpb[:s0 + c], pos, 1 / math.sqrt(128))
     assert_within_tolerance(st["attn"], att.reshape(c, -1), "attention")
-    assert_within_tolerance(st["o"], oracle.gemm(st["attn"], w["w_o"]), "o")
-    assert_bitwise(st["h"], oracle.residual_add(xr, st["o"]), "h")
-    assert_within_tolerance(st["n2"], oracle.rmsnorm(st["h"], w["gamma2"], 1e-6), "n2")
-    assert_within_tolerance(st["gu"], oracle.gemm(st["n2"], w["w_gate_up"]), "gate/up")
-    assert_within_tolerance(st["act"], oracle.swiglu(st["gu"][:, :9728], st["gu"][:, 9728:]), "swiglu")
-    assert_within_tolerance(st["d"], oracle.gemm(st["act"], w["w_down"]), "down")
-    assert_bitwise(y[s0:], oracle.residual_add(st["h"], st["d"]), "y")
+    bf = lambda a, wt: bi.gemm(a, wt)
+    check_fused_stages(xr, st, y[s0:], bf, {k: dev(w[k]) for k in ("w_o", "w_gate_up", "w_down")}, w, 9728)
     # end to end over both chunks
     kpo = np.zeros((T, 8, 128), np.uint16); vpo = np.zeros_like(kpo)
     ref = oracle.block_forward(cfg, w, x, [dict(q_len=T, ctx_len=0, kv_base=0)], kpo, vpo)
@@ -262,10 +281,11 @@ def test_int4_mixed_step_parity_sampled(int4_block):
     deq = {k: oracle.dequant_int4_g32(*w[k]) for k in ("w_qkv", "w_o", "w_gate_up", "w_down")}
     assert_within_tolerance(st["n1"][rows], oracle.rmsnorm(x[rows], w["gamma1"], 1e-6), "n1")
     assert_within_tolerance(st["qkv"][rows], oracle.gemm(st["n1"][rows], deq["w_qkv"]), "qkv (int4)")
-    assert_within_tolerance(st["o"][rows], oracle.gemm(st["attn"][rows], deq["w_o"]), "o (int4)")
-    assert_within_tolerance(st["gu"][rows], oracle.gemm(st["n2"][rows], deq["w_gate_up"]), "gate/up (int4)")
-    assert_within_tolerance(st["d"][rows], oracle.gemm(st["act"][rows], deq["w_down"]), "down (int4)")
-    assert_bitwise(yb[rows], oracle.residual_add(st["h"][rows], st["d"][rows]), "y")
+    q4 = {k: (torch.from_numpy(w[k][0]).cuda(), torch.from_numpy(w[k][1].view(np.int16)).cuda())
+          for k in ("w_o", "w_gate_up", "w_down")}
+    w4 = lambda a, wt: bi.gemm_w4(a, *wt)
+    sub = {k: v[rows] for k, v in st.items()}
+    check_fused_stages(x[rows], sub, yb[rows], w4, q4, dict(deq, gamma2=w["gamma2"]), 12288, " (int4)")
     # attention of decode rows 0, 5 and prefill rows, against the GPU's own cache contents
     kpb_rows = lambda b, L: (bits(kp[b * cap:b * cap + L]), bits(vp[b * cap:b * cap + L]))
     q = st["q"].reshape(M, 32, 128)

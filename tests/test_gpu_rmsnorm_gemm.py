@@ -1,4 +1,5 @@
-"""GPU parity and invariance of bi_rmsnorm, bi_gemm and bi_gemm_w4 (through the C-ABI).
+"""GPU parity and invariance of bi_rmsnorm, bi_gemm and bi_gemm_w4, and the fused
+GEMM epilogues (residual add, SwiGLU) (through the C-ABI).
 
 Parity: each output element within |gpu - oracle| <= 8e-3 |oracle| + 1e-3;
 bitwise where the mathematics fixes the bits (constant rows, small-integer
@@ -179,3 +180,41 @@ def test_gemm_w4_batch_invariance():
         announce("gemm_w4 invariance", M)
         idx = rng.choice(2304, size=M, replace=False)
         assert_bitwise(bits(bi.gemm_w4(dev(A[idx]), wqd, wsd)), ref[idx], f"gemm_w4 M={M}")
+
+
+# ------------------------------------------------------- fused epilogues
+@pytest.mark.parametrize("m,n,k", [(1, 768, 256), (77, 2560, 1024), (300, 520, 320), (513, 4096, 4096)])
+def test_gemm_residual_equals_gemm_then_add(m, n, k):
+    device()
+    announce("gemm + residual", m, n, k)
+    a = dev(synth.normal_bf16(5000 + m, (m, k)))
+    w = dev(synth.normal_bf16(5001 + n, (n, k), 0.02))
+    r = dev(synth.normal_bf16(5002 + k, (m, n)))
+    ref = bits(bi.add(r, bi.gemm(a, w)))
+    assert_bitwise(bits(bi.gemm_residual(a, w, r)), ref, "bf16 fused residual")
+    r2 = r.clone()
+    bi.gemm_residual(a, w, r2, out=r2)  # in place over the residual
+    assert_bitwise(bits(r2), ref, "bf16 fused residual in place")
+    wq, ws = synth.quantize_int4_g32(5003 + n, n, k)
+    wq, ws = torch.from_numpy(wq).cuda(), torch.from_numpy(ws.view("int16")).cuda()
+    ref4 = bits(bi.add(r, bi.gemm_w4(a, wq, ws)))
+    assert_bitwise(bits(bi.gemm_w4_residual(a, wq, ws, r)), ref4, "int4 fused residual")
+
+
+@pytest.mark.parametrize("m,f,k", [(1, 128, 256), (77, 640, 1024), (300, 9728, 2560), (513, 12288, 4096)])
+def test_gemm_swiglu_equals_gemm_then_swiglu(m, f, k):
+    device()
+    announce("gemm + swiglu", m, f, k)
+    a = dev(synth.normal_bf16(5100 + m, (m, k)))
+    w = dev(synth.normal_bf16(5101 + f, (2 * f, k), 0.02))
+    ref = bits(bi.swiglu(bi.gemm(a, w)))
+    got = bits(bi.gemm_swiglu(a, w))
+    assert_bitwise(got, ref, "bf16 fused swiglu")
+    wq, ws = synth.quantize_int4_g32(5102 + f, 2 * f, k)
+    wq, ws = torch.from_numpy(wq).cuda(), torch.from_numpy(ws.view("int16")).cuda()
+    ref4 = bits(bi.swiglu(bi.gemm_w4(a, wq, ws)))
+    assert_bitwise(bits(bi.gemm_w4_swiglu(a, wq, ws)), ref4, "int4 fused swiglu")
+    # rows of the fused form do not depend on the batch either
+    if m > 1:
+        one = bits(bi.gemm_w4_swiglu(a[m - 1:m], wq, ws))
+        assert_bitwise(one[0], ref4[m - 1], "fused swiglu row alone")
