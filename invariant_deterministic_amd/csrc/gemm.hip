@@ -58,6 +58,23 @@ constexpr int TILE = BM * BK;           // bf16 elements of one operand tile (BM
 constexpr int kStoreAfter = 2;         // the next stage is written to LDS after this substep's MFMAs
 static_assert(BM == BN, "square tile assumed by the LDS layout");
 
+// Work-group -> tile.  Work-groups are dealt round-robin to the 8 XCDs (work-group
+// wg runs on XCD wg % 8), each XCD has its own L2.  Tiles are put in a grouped
+// order -- kTileGroup tile rows at a time, column by column inside the group -- and
+// each XCD takes a contiguous run of that order, so the ~32 tiles an XCD runs at
+// once span a few tile rows and a few tile columns and share both their A and their
+// W slices in that L2.  Only whole tiles move between work-groups: no element's
+// arithmetic depends on this.
+constexpr int kTileGroup = 4;
+__device__ __forceinline__ int tile_of(int wg, int n_tiles, int tiles_n) {
+  const int q = n_tiles / 8, r = n_tiles % 8, x = wg % 8;
+  const int i = x * q + min(x, r) + wg / 8;  // XCD x holds q (+1 if x < r) consecutive positions
+  const int tiles_m = n_tiles / tiles_n;
+  const int g = i / (kTileGroup * tiles_n), rem = i % (kTileGroup * tiles_n);
+  const int rows = min(kTileGroup, tiles_m - g * kTileGroup);
+  return (g * kTileGroup + rem % rows) * tiles_n + rem / rows;
+}
+
 // Element offset of 16-byte chunk `chunk` (0..7) of tile row `row`.  LDS
 // serves 16 lanes of a 16-byte access per cycle from 64 four-byte banks, i.e.
 // two 128-byte rows; keying the xor on row / 2 puts the 16 rows a fragment
@@ -161,11 +178,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
                                                      int tiles_n, int n_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];
 
-  // Work-group -> tile.  Work-groups are dealt round-robin to the 8 XCDs;
-  // give each XCD a contiguous run of row-major tiles so tiles sharing A rows
-  // share an L2.  This only moves whole tiles between work-groups.
-  const int wg = blockIdx.x;
-  const int tile = (n_tiles % 8 == 0) ? (wg % 8) * (n_tiles / 8) + wg / 8 : wg;
+  const int tile = tile_of(blockIdx.x, n_tiles, tiles_n);
   const int tm = tile / tiles_n;
   const int tn = tile % tiles_n;
 
@@ -345,8 +358,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
   __shared__ __attribute__((aligned(1024))) uint16_t sW0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sW1[TILE];
 
-  const int wg = blockIdx.x;
-  const int tile = (n_tiles % 8 == 0) ? (wg % 8) * (n_tiles / 8) + wg / 8 : wg;
+  const int tile = tile_of(blockIdx.x, n_tiles, tiles_n);
   const int tm = tile / tiles_n;
   const int tn = tile % tiles_n;
 
