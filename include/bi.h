@@ -150,7 +150,9 @@ bi_status bi_swiglu(const bi_bf16* gu, bi_bf16* act, int64_t rows, int64_t F, hi
  * the rotation (plain copy).
  *   pos [rows] int32 device, >= 0;  kv_row [rows] int64 device, row index
  *   into the pools k_pool, v_pool [*, Hkv, D] bf16.  D in {64, 128};
- *   Hq % Hkv == 0.                                                          */
+ *   Hq % Hkv == 0.  The pools' sizes are not passed: every kv_row[r] must
+ *   name a row of the pools (bi_block_forward checks its rows against
+ *   bi_kv_pool.rows before any launch).                                     */
 bi_status bi_rope_kv(const bi_bf16* qkv, const int32_t* pos, const int64_t* kv_row,
                      bi_bf16* q_out, bi_bf16* k_pool, bi_bf16* v_pool,
                      int64_t rows, int Hq, int Hkv, int D, double theta, hipStream_t stream);

@@ -172,6 +172,18 @@ def _dev(t: torch.Tensor, dtype, name):
     return t
 
 
+def _out(out, shape, dtype, like, name="out"):
+    """A new output tensor, or the caller's after checking it: same device kind, dtype,
+    contiguity and exact shape (the kernels write exactly that many elements)."""
+    shape = tuple(int(v) for v in shape)
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _dev(out, dtype, name)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"{name}: shape {tuple(out.shape)}, expected {shape}")
+    return out
+
+
 BF16 = torch.bfloat16
 HALF_BITS = (torch.float16, torch.int16)
 
@@ -180,7 +192,7 @@ HALF_BITS = (torch.float16, torch.int16)
 def rmsnorm(x, gamma, eps: float, out=None):
     _dev(x, BF16, "x"); _dev(gamma, BF16, "gamma")
     rows, hidden = x.shape
-    out = torch.empty_like(x) if out is None else _dev(out, BF16, "out")
+    out = _out(out, x.shape, BF16, x)
     _check(lib().bi_rmsnorm(_ptr(x), _ptr(gamma), _ptr(out), rows, hidden, eps, _stream()), "bi_rmsnorm")
     return out
 
@@ -191,7 +203,7 @@ def gemm(A, W, out=None):
     N = W.shape[0]
     if W.shape[1] != K:
         raise ValueError("K mismatch")
-    out = torch.empty((M, N), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    out = _out(out, (M, N), BF16, A)
     _check(lib().bi_gemm(_ptr(A), _ptr(W), _ptr(out), M, N, K, _stream()), "bi_gemm")
     return out
 
@@ -202,7 +214,7 @@ def gemm_w4(A, Wq, Ws, out=None):
     N = Wq.shape[0]
     if Wq.shape[1] * 2 != K or Ws.shape != (N, K // 32):
         raise ValueError("int4 weight shape mismatch")
-    out = torch.empty((M, N), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    out = _out(out, (M, N), BF16, A)
     _check(lib().bi_gemm_w4(_ptr(A), _ptr(Wq), _ptr(Ws), _ptr(out), M, N, K, _stream()), "bi_gemm_w4")
     return out
 
@@ -214,7 +226,7 @@ def gemm_residual(A, W, R, out=None):
     N = W.shape[0]
     if W.shape[1] != K or R.shape != (M, N):
         raise ValueError("shape mismatch")
-    out = torch.empty((M, N), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    out = _out(out, (M, N), BF16, A)
     _check(lib().bi_gemm_residual(_ptr(A), _ptr(W), _ptr(R), _ptr(out), M, N, K, _stream()), "bi_gemm_residual")
     return out
 
@@ -226,7 +238,7 @@ def gemm_swiglu(A, W, out=None):
     F = W.shape[0] // 2
     if W.shape[1] != K or W.shape[0] != 2 * F:
         raise ValueError("shape mismatch")
-    out = torch.empty((M, F), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    out = _out(out, (M, F), BF16, A)
     _check(lib().bi_gemm_swiglu(_ptr(A), _ptr(W), _ptr(out), M, F, K, _stream()), "bi_gemm_swiglu")
     return out
 
@@ -237,7 +249,7 @@ def gemm_w4_residual(A, Wq, Ws, R, out=None):
     N = Wq.shape[0]
     if Wq.shape[1] * 2 != K or Ws.shape != (N, K // 32) or R.shape != (M, N):
         raise ValueError("shape mismatch")
-    out = torch.empty((M, N), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    out = _out(out, (M, N), BF16, A)
     _check(lib().bi_gemm_w4_residual(_ptr(A), _ptr(Wq), _ptr(Ws), _ptr(R), _ptr(out), M, N, K, _stream()),
            "bi_gemm_w4_residual")
     return out
@@ -249,14 +261,16 @@ def gemm_w4_swiglu(A, Wq, Ws, out=None):
     F = Wq.shape[0] // 2
     if Wq.shape[1] * 2 != K or Ws.shape != (2 * F, K // 32) or Wq.shape[0] != 2 * F:
         raise ValueError("shape mismatch")
-    out = torch.empty((M, F), dtype=BF16, device=A.device) if out is None else _dev(out, BF16, "out")
+    out = _out(out, (M, F), BF16, A)
     _check(lib().bi_gemm_w4_swiglu(_ptr(A), _ptr(Wq), _ptr(Ws), _ptr(out), M, F, K, _stream()), "bi_gemm_w4_swiglu")
     return out
 
 
 def add(x, o, out=None):
     _dev(x, BF16, "x"); _dev(o, BF16, "o")
-    out = torch.empty_like(x) if out is None else _dev(out, BF16, "out")
+    if o.shape != x.shape:
+        raise ValueError("x and o shapes differ")
+    out = _out(out, x.shape, BF16, x)
     _check(lib().bi_add(_ptr(x), _ptr(o), _ptr(out), x.numel(), _stream()), "bi_add")
     return out
 
@@ -265,7 +279,7 @@ def swiglu(gu, out=None):
     _dev(gu, BF16, "gu")
     rows, two_f = gu.shape
     F = two_f // 2
-    out = torch.empty((rows, F), dtype=BF16, device=gu.device) if out is None else _dev(out, BF16, "out")
+    out = _out(out, (rows, F), BF16, gu)
     _check(lib().bi_swiglu(_ptr(gu), _ptr(out), rows, F, _stream()), "bi_swiglu")
     return out
 
@@ -274,7 +288,9 @@ def rope_kv(qkv, pos, kv_row, k_pool, v_pool, Hq, Hkv, D, theta, q_out=None):
     _dev(qkv, BF16, "qkv"); _dev(pos, torch.int32, "pos"); _dev(kv_row, torch.int64, "kv_row")
     _dev(k_pool, BF16, "k_pool"); _dev(v_pool, BF16, "v_pool")
     rows = qkv.shape[0]
-    q_out = torch.empty((rows, Hq * D), dtype=BF16, device=qkv.device) if q_out is None else q_out
+    if qkv.dim() != 2 or qkv.shape[1] != (Hq + 2 * Hkv) * D or pos.shape != (rows,) or kv_row.shape != (rows,):
+        raise ValueError("qkv / pos / kv_row shapes do not match rows, Hq, Hkv, D")
+    q_out = _out(q_out, (rows, Hq * D), BF16, qkv, "q_out")
     _check(lib().bi_rope_kv(_ptr(qkv), _ptr(pos), _ptr(kv_row), _ptr(q_out), _ptr(k_pool), _ptr(v_pool),
                             rows, Hq, Hkv, D, float(theta), _stream()), "bi_rope_kv")
     return q_out
@@ -285,7 +301,7 @@ def attn_prefill(q, k_cache, v_cache, q_start, Hq, Hkv, D, scale, out=None):
     T = q.shape[0]
     if k_cache.shape[0] < q_start + T:
         raise ValueError("cache shorter than q_start + T")
-    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    out = _out(out, q.shape, BF16, q)
     _check(lib().bi_attn_prefill(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), int(q_start), T,
                                  Hq, Hkv, D, float(scale), _stream()), "bi_attn_prefill")
     return out
@@ -302,7 +318,7 @@ def attn_decode(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq, Hkv, D, scal
     need = attn_decode_workspace(B, max_kv_len, Hq, D)
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
-    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    out = _out(out, q.shape, BF16, q)
     _check(lib().bi_attn_decode(_ptr(q), _ptr(k_all), _ptr(v_all), _ptr(kv_offset), _ptr(kv_len), B,
                                 int(max_kv_len), Hq, Hkv, D, float(scale), _ptr(ws), ws.numel(), _ptr(out),
                                 _stream()), "bi_attn_decode")
@@ -316,7 +332,7 @@ def attn_decode_prefill_order(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq
     if order is not None:
         _dev(order, torch.int32, "order")
     B = q.shape[0]
-    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    out = _out(out, q.shape, BF16, q)
     _check(lib().bi_attn_decode_prefill_order(_ptr(q), _ptr(k_all), _ptr(v_all), _ptr(kv_offset), _ptr(kv_len),
                                               _ptr(order), B, int(max_kv_len), Hq, Hkv, D, float(scale),
                                               _ptr(out), _stream()), "bi_attn_decode_prefill_order")
@@ -347,7 +363,7 @@ def kv_append_q8(pool, k, v, dst_row):
 def attn_prefill_paged_q8(q, pool, block_table, q_start, Hq, scale, out=None):
     _dev(q, BF16, "q"); _dev(block_table, torch.int32, "block_table")
     T = q.shape[0]
-    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    out = _out(out, q.shape, BF16, q)
     _check(lib().bi_attn_prefill_paged_q8(_ptr(q), _ptr(pool.k), _ptr(pool.v), _ptr(pool.ks), _ptr(pool.vs),
                                           _ptr(block_table), _ptr(out), int(q_start), T, Hq, pool.Hkv, pool.D,
                                           float(scale), _stream()), "bi_attn_prefill_paged_q8")
@@ -359,7 +375,7 @@ def attn_decode_paged_q8(q, pool, block_tables, kv_len, max_kv_len, Hq, scale, o
     if order is not None:
         _dev(order, torch.int32, "order")
     B = q.shape[0]
-    out = torch.empty_like(q) if out is None else _dev(out, BF16, "out")
+    out = _out(out, q.shape, BF16, q)
     _check(lib().bi_attn_decode_paged_q8(_ptr(q), _ptr(pool.k), _ptr(pool.v), _ptr(pool.ks), _ptr(pool.vs),
                                          _ptr(block_tables), block_tables.shape[1], _ptr(kv_len), _ptr(order), B,
                                          int(max_kv_len), Hq, pool.Hkv, pool.D, float(scale), _ptr(out), _stream()),
@@ -376,7 +392,7 @@ def sample(logits, seeds, positions, temperature=0.0, top_k=1, top_p=1.0, min_p=
     if history is not None:
         _dev(history, torch.int32, "history")
         n_hist = history.shape[1]
-    out = torch.empty(rows, dtype=torch.int32, device=logits.device) if out is None else out
+    out = _out(out, (rows,), torch.int32, logits)
     prm = bi_sampling(temperature, top_k, top_p, min_p, repeat, presence, frequency)
     _check(lib().bi_sample(_ptr(logits), rows, vocab, ctypes.byref(prm), _ptr(seeds), _ptr(positions), _ptr(history),
                            n_hist, _ptr(out), _stream()), "bi_sample")
@@ -387,7 +403,7 @@ def token_hash(ids, offsets, counts, out=None):
     """BLAKE3 of each sequence's int32 ids (device); returns uint8 [n_seqs, 32]."""
     _dev(ids, torch.int32, "ids"); _dev(offsets, torch.int64, "offsets"); _dev(counts, torch.int32, "counts")
     n = counts.shape[0]
-    out = torch.empty((n, 32), dtype=torch.uint8, device=ids.device) if out is None else out
+    out = _out(out, (n, 32), torch.uint8, ids)
     _check(lib().bi_token_hash(_ptr(ids), _ptr(offsets), _ptr(counts), n, _ptr(out), _stream()), "bi_token_hash")
     return out
 

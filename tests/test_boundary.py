@@ -68,6 +68,29 @@ def test_gemm_checks():
     assert L.bi_gemm_w4(P16, P16b, P16c, P16, 1, 8, 32, NUL) == UNSUP
 
 
+def test_fused_gemm_checks():
+    L = bi.lib()
+    P4 = ctypes.c_void_p(0x400000)
+    # residual forms: R is checked like the other operands
+    assert L.bi_gemm_residual(P16, P16b, NUL, P16c, 1, 8, 64, NUL) == NULL
+    assert L.bi_gemm_residual(P16, P16b, MIS, P16c, 1, 8, 64, NUL) == ALIGN
+    assert L.bi_gemm_residual(P16, P16b, P4, P16c, 0, 8, 64, NUL) == SHAPE
+    assert L.bi_gemm_residual(P16, P16b, P4, P16c, 1, 12, 64, NUL) == UNSUP
+    assert L.bi_gemm_w4_residual(P16, P16b, NUL, P4, P16c, 1, 8, 64, NUL) == NULL
+    assert L.bi_gemm_w4_residual(P16, P16b, P16c, NUL, P4, 1, 8, 64, NUL) == NULL
+    assert L.bi_gemm_w4_residual(P16, P16b, ctypes.c_void_p(0x500001), P4, P16c, 1, 8, 64, NUL) == ALIGN
+    assert L.bi_gemm_w4_residual(P16, P16b, P16c, MIS, P4, 1, 8, 64, NUL) == ALIGN
+    # SwiGLU forms: F outputs from 2F weight rows, F a multiple of the 128-column pair tile
+    assert L.bi_gemm_swiglu(NUL, P16b, P16c, 1, 128, 64, NUL) == NULL
+    assert L.bi_gemm_swiglu(P16, P16b, P16c, 1, 0, 64, NUL) == SHAPE
+    assert L.bi_gemm_swiglu(P16, P16b, P16c, 1, 120, 64, NUL) == UNSUP
+    assert L.bi_gemm_swiglu(P16, P16b, P16c, 1, 128, 96, NUL) == UNSUP
+    assert L.bi_gemm_swiglu(P16, P16b, MIS, 1, 128, 64, NUL) == ALIGN
+    assert L.bi_gemm_w4_swiglu(P16, P16b, NUL, P16c, 1, 128, 64, NUL) == NULL
+    assert L.bi_gemm_w4_swiglu(P16, P16b, P4, P16c, 1, 64, 64, NUL) == UNSUP
+    assert L.bi_gemm_w4_swiglu(P16, P16b, ctypes.c_void_p(0x500001), P16c, 1, 128, 64, NUL) == ALIGN
+
+
 def test_attention_checks():
     L = bi.lib()
     sc = 0.088
