@@ -282,17 +282,21 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     f32x16 s;
     bf16x8 p_hi[2], p_lo[2];
     for (int blk = 0; blk <= n_blk; ++blk) {
-      // ---- MFMA phase
+      // ---- MFMA phase, at raised wave priority: the SIMD's other wave is in its VALU
+      // phase, and this wave's MFMAs and fragment reads go first
+      __builtin_amdgcn_s_setprio(1);
       if (blk < nb_w) {
         // S^T: keys 32 kh .. 32 kh + 31 of the block, queries of the wave
         const uint16_t* cK = sKV[0][blk % NS];
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        // every K fragment is read before the chain of MFMAs starts
+        bf16x8 kf[KK];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cK + k_off<D>(32 * kh + l32, 2 * kk + hf));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
-        }
+        for (int kk = 0; kk < KK; ++kk)
+          kf[kk] = *reinterpret_cast<const bf16x8*>(cK + k_off<D>(32 * kh + l32, 2 * kk + hf));
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk], qf[kk], s, 0, 0, 0);
       }
       if (blk >= 1 && blk - 1 < nb_w) {
         // O^T[d][q] += V^T[d][key] P^T[key][q] for block blk - 1, P = hi + lo in bf16.  MFMA
@@ -318,6 +322,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         }
       }
       if (blk + 2 < n_blk) store_block((blk + 2) % NS);
+      __builtin_amdgcn_s_setprio(0);
       __syncthreads();
       // ---- VALU phase
       if (blk + 3 < n_blk) load_block(blk + 3);
