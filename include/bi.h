@@ -74,8 +74,15 @@ const char* bi_build_id(void);
 int bi_kv_split_size(void);
 
 /* Compile-time tile shape of bi_gemm / bi_gemm_w4 (the same for every M):
- * writes BM, BN, BK into out[0..2]. */
+ * writes BM, BN, BK into out[0..2] (256, 256, 64). */
 void bi_gemm_tile(int out[3]);
+
+/* Column-tile width the GEMMs use for a weight of N rows: 256, or 192 for
+ * bf16 weights (weight_format BI_WEIGHTS_BF16) of at most 3072 rows, where
+ * 256-wide tiles would leave most compute units idle.  A function of the
+ * weight alone, never of M; the SwiGLU forms always pair 128 gate and 128 up
+ * rows per tile.  Returns 0 for N < 1.  (No element's bits depend on it.)   */
+int bi_gemm_tile_cols(int64_t N, int weight_format);
 
 /* ------------------------------------------------------------------ RMSNorm
  * y[r, j] = bf16( x[r, j] * rsqrt(sum_j x[r, j]^2 / hidden + eps) * gamma[j] )
@@ -89,11 +96,11 @@ bi_status bi_rmsnorm(const bi_bf16* x, const bi_bf16* gamma, bi_bf16* y,
 
 /* --------------------------------------------------------------------- GEMM
  * C = A * W^T, fp32 accumulation, bf16 output (M-0002 `technical`: matrix
- * multiplication).  One tile shape for every M (see bi_gemm_tile), no
- * split-K: each C[i, j] is accumulated over k = 0..K-1 in the same order for
- * every M and every position of row i.
+ * multiplication).  One tile shape for every M (see bi_gemm_tile and
+ * bi_gemm_tile_cols), no split-K: each C[i, j] is accumulated over
+ * k = 0..K-1 in the same order for every M and every position of row i.
  *   A [M, K] bf16   W [N, K] bf16   C [M, N] bf16 (must not alias A or W)
- *   M >= 1; N >= 8, N % 8 == 0; K >= 64, K % 64 == 0.                        */
+ *   M >= 1; N >= 8, N % 8 == 0; K >= 64, K % 64 == 0, K <= 2^22.            */
 bi_status bi_gemm(const bi_bf16* A, const bi_bf16* W, bi_bf16* C,
                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
@@ -116,7 +123,8 @@ bi_status bi_gemm_w4(const bi_bf16* A, const uint8_t* Wq, const bi_f16* Ws, bi_b
  *   bi_gemm_swiglu:    act[m, j] = bf16(silu(g) u), g = bf16((A W^T)[m, j]),
  *                      u = bf16((A W^T)[m, F + j]) for W [2F, K] (gate rows,
  *                      then up rows); act [M, F] bf16, F % 128 == 0 (the
- *                      tile pairs gate and up columns of the same outputs);
+ *                      tile pairs gate and up columns of the same outputs)
+ *                      and (F + 128) K 2 < 2^32 (bf16 weights);
  *   _w4 forms: W given as int4 codes and fp16 scales as for bi_gemm_w4.
  * Other size rules as bi_gemm (for bi_gemm_swiglu with N = 2F).              */
 bi_status bi_gemm_residual(const bi_bf16* A, const bi_bf16* W, const bi_bf16* R, bi_bf16* C,

@@ -72,6 +72,7 @@ _SIGNATURES = {
     "bi_build_id": (ctypes.c_char_p, []),
     "bi_kv_split_size": (c_int, []),
     "bi_gemm_tile": (None, [ctypes.POINTER(c_int)]),
+    "bi_gemm_tile_cols": (c_int, [c_int64, c_int]),
     "bi_rmsnorm": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_float, c_void_p]),
     "bi_gemm": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
     "bi_gemm_w4": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p]),
@@ -150,6 +151,11 @@ def gemm_tile():
     arr = (c_int * 3)()
     lib().bi_gemm_tile(arr)
     return tuple(arr)
+
+
+def gemm_tile_cols(N: int, int4_weights: bool = False) -> int:
+    """Column-tile width the GEMMs use for a weight of N rows (a function of N alone)."""
+    return int(lib().bi_gemm_tile_cols(int(N), 1 if int4_weights else 0))
 
 
 def _stream():

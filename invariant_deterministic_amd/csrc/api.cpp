@@ -46,10 +46,10 @@ bi_status check_gemm(const void* A, const void* W, const void* C, int64_t M, int
   if (!A || !W || !C) return BI_ERR_NULL;
   if (M < 1 || N < 1 || K < 1) return BI_ERR_SHAPE;
   if (N % 8 || K % bi::kGemmBK) return BI_ERR_UNSUPPORTED;
-  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX || M * K > (int64_t(1) << 40) ||
+  if (M > INT32_MAX || N > INT32_MAX || K > bi::kGemmMaxK || M * K > (int64_t(1) << 40) ||
       M * N > (int64_t(1) << 40))
     return BI_ERR_UNSUPPORTED;
-  const int64_t tiles = ((M + bi::kGemmBM - 1) / bi::kGemmBM) * ((N + bi::kGemmBN - 1) / bi::kGemmBN);
+  const int64_t tiles = ((M + bi::kGemmBM - 1) / bi::kGemmBM) * ((N + bi::kGemmBNNarrow - 1) / bi::kGemmBNNarrow);
   if (tiles > INT32_MAX) return BI_ERR_UNSUPPORTED;
   if (!aligned16(A) || !aligned16(W) || !aligned16(C)) return BI_ERR_ALIGN;
   return BI_OK;
@@ -151,7 +151,12 @@ bi_status check_weight(const bi_weight& w, int fmt) {
 }
 
 // the gate/up GEMM carries SwiGLU in its epilogue when its tile can pair the columns
-bool ffn_fused(const bi_block_cfg& c) { return c.ffn % 128 == 0; }
+// The gated gate/up GEMM (SwiGLU in its epilogue) needs F % 128 == 0; with bf16 weights its
+// operand offsets, 32-bit from the tile's first gate row, reach (F + 128) rows of W.
+bool gated_ok(int64_t F, int64_t K, bool bf16_weights) {
+  return F % 128 == 0 && (!bf16_weights || (F + 128) * K * 2 < (int64_t(1) << 32));
+}
+bool ffn_fused(const bi_block_cfg& c) { return gated_ok(c.ffn, c.hidden, c.weight_format == BI_WEIGHTS_BF16); }
 
 struct WsLayout {
   bi_block_ws_layout pub;
@@ -237,6 +242,11 @@ void bi_gemm_tile(int out[3]) {
   out[2] = bi::kGemmBK;
 }
 
+int bi_gemm_tile_cols(int64_t N, int weight_format) {
+  if (N < 1) return 0;
+  return weight_format == BI_WEIGHTS_BF16 ? bi::gemm_tile_n(N, bi::kEpiPlain) : bi::kGemmBN;
+}
+
 bi_status bi_rmsnorm(const bi_bf16* x, const bi_bf16* gamma, bi_bf16* y, int64_t rows,
                      int64_t hidden, float eps, hipStream_t stream) {
   const bi_status st = check_rmsnorm(x, gamma, y, rows, hidden, eps);
@@ -275,7 +285,7 @@ bi_status bi_gemm_swiglu(const bi_bf16* A, const bi_bf16* W, bi_bf16* act, int64
   if (F < 1) return BI_ERR_SHAPE;
   const bi_status st = check_gemm(A, W, act, M, 2 * F, K);
   if (st != BI_OK) return st;
-  if (F % 128) return BI_ERR_UNSUPPORTED;
+  if (!gated_ok(F, K, true)) return BI_ERR_UNSUPPORTED;
   return from_hip(bi::launch_gemm_ex(A, W, nullptr, act, M, F, K, bi::kEpiGated, stream));
 }
 

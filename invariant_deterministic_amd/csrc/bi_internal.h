@@ -9,10 +9,17 @@
 
 namespace bi {
 
-// GEMM tile shape: one shape for every M (no split-K).
+// GEMM tile shape: one shape for every M (no split-K).  bf16 weights of at most
+// kGemmNarrowN rows (outside the gated form) use kGemmBNNarrow-wide column tiles.
 constexpr int kGemmBM = 256;
 constexpr int kGemmBN = 256;
 constexpr int kGemmBK = 64;
+constexpr int kGemmBNNarrow = 192;
+constexpr int64_t kGemmNarrowN = 3072;
+// operand offsets of the bf16 schedule are 32-bit from the tile's first rows
+constexpr int64_t kGemmMaxK = int64_t(1) << 22;
+// column-tile width of the bf16 GEMM for a weight of N rows (epi: kEpi*)
+int gemm_tile_n(int64_t N, int epi);
 
 // Decode attention: fixed key/value split size.
 constexpr int kKvSplit = 256;

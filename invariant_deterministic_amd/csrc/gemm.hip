@@ -4,10 +4,12 @@
 // Matrix multiplication is one of the operations the M-0002 record
 // ("Deterministic and bit-exact inference", field `technical`) makes
 // batch-invariant.  The invariance argument here:
-//  * one tile shape (256 x 256 x 64) and one instruction stream for every M:
-//    there is no M-dependent dispatch, no split-K and no stream-K, and rows
-//    past M are handled by clamping their loads and masking their stores in
-//    the same instruction stream;
+//  * one tile shape and one instruction stream for every M: 256 x 256 x 64, or
+//    256 x 192 x 64 for bf16 weights of at most 3072 rows (the width is a
+//    function of the weight's row count alone); there is no M-dependent
+//    dispatch, no split-K and no stream-K, and rows past M are handled by
+//    clamping their loads and masking their stores in the same instruction
+//    stream;
 //  * each C[i, j] is accumulated by one lane of one MFMA chain: K is walked in
 //    64-wide steps in ascending order, each step as four 16-deep
 //    v_mfma_f32_32x32x16_bf16 instructions in ascending order;
@@ -22,7 +24,8 @@
 // -- straight into the same LDS tile the bf16 path uses, so the int4 GEMM is
 // bit-identical to the bf16 GEMM on the de-quantised weight.
 //
-// Data flow: global -> registers (prefetch of step k+1 during step k) -> LDS
+// Int4 weights, register-staged schedule.  Data flow: global -> registers
+// (prefetch of step k+1 during step k) -> LDS
 // (two stages, 16-byte chunks xor-swizzled by row pair to keep ds_read_b128
 // and ds_write_b128 conflict-free) -> MFMA operands.  Step k+1's registers go
 // into the free LDS stage in the middle of step k's MFMA stream (after its
@@ -35,15 +38,16 @@
 // 4 consecutive output columns of one output row and stores them as one
 // 8-byte write.
 //
-// bf16 weights use a second schedule of the same tile and the same per-element
-// MFMA chain (so the same bits): the eight waves form two groups of four, one
+// bf16 weights use a second schedule with the same per-element MFMA chain (so
+// the same bits): the eight waves form two groups of four, one
 // wave of each group per SIMD, that take turns -- while one group issues the
 // 16 MFMAs of half a stage from registers, the other reads its next
 // half-stage's fragments from LDS -- separated by work-group barriers, group 1
 // one barrier behind group 0.  Both operand tiles go from global memory
 // straight into LDS (global_load_lds_dwordx4, no staging registers), a stage
 // ahead, each LDS stage a separate array so the compiler can tell the pending
-// loads from the reads.
+// loads from the reads.  Operand offsets are 32-bit and relative to the tile's
+// first rows, so one schedule serves every operand size.
 #include <type_traits>
 
 #include "bi_dev.h"
@@ -113,18 +117,20 @@ __device__ __forceinline__ void dequant_group_to_lds(const uint4& rq, uint16_t r
 // element's MFMA chain is the same as in the plain GEMM: the bits of the fused forms equal
 // the GEMM followed by the elementwise kernel.
 // W row behind tile row t of column tile tn (F: the gated GEMM's output width)
-template <int EPI>
+template <int EPI, int BNT = BN>
 __device__ __forceinline__ int w_row(int tn, int t, int F) {
   if constexpr (EPI == kEpiGated) return ((t >> 6) & 1) * F + tn * 128 + ((t >> 7) << 6) + (t & 63);
-  else return tn * BN + t;
+  else return tn * BNT + t;
 }
 
-// acc[bn][bm][r] is tile element (row wm*64 + bm*32 + (lane & 31), column wn*128 + bn*32 +
-// 8*(r/4) + 4*(lane/32) + r%4); C has N columns (the gated form: N = F outputs)
-template <int EPI>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], uint16_t* __restrict__ C,
+// acc[bn][bm][r] is tile element (row wm*64 + bm*32 + (lane & 31), column wn*(BNT/2) + bn*32 +
+// 8*(r/4) + 4*(lane/32) + r%4) of a BM x BNT tile; C has N columns (the gated form: N = F
+// outputs, BNT = 256)
+template <int EPI, int BNT>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BNT / 64][2], uint16_t* __restrict__ C,
                                            const uint16_t* __restrict__ R, int M, int N, int tm, int tn,
                                            int wm, int wn, int lane) {
+  static_assert(EPI != kEpiGated || BNT == 256, "the gated epilogue pairs 128-column halves of a 256 tile");
 #pragma unroll
   for (int bm = 0; bm < 2; ++bm) {
     const int m = tm * BM + wm * 64 + bm * 32 + (lane & 31);
@@ -148,10 +154,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], uint16_t* 
       }
     } else {
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn) {
+      for (int bn = 0; bn < BNT / 64; ++bn) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int n = tn * BN + wn * 128 + bn * 32 + 8 * q + 4 * (lane >> 5);
+          const int n = tn * BNT + wn * (BNT / 2) + bn * 32 + 8 * q + 4 * (lane >> 5);
           if (n < N) {
             uint2 v;
             v.x = pack2bf(acc[bn][bm][4 * q + 0], acc[bn][bm][4 * q + 1]);
@@ -169,13 +175,14 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][2], uint16_t* 
   }
 }
 
-template <bool W4, int EPI>
-__global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict__ A,
-                                                     const void* __restrict__ Wv,
-                                                     const uint16_t* __restrict__ Ws,
-                                                     const uint16_t* __restrict__ R,
-                                                     uint16_t* __restrict__ C, int M, int N, int K,
-                                                     int tiles_n, int n_tiles) {
+// int4-weight GEMM, register-staged schedule (see the file comment).
+template <int EPI>
+__global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restrict__ A,
+                                                        const uint8_t* __restrict__ Wq,
+                                                        const uint16_t* __restrict__ Ws,
+                                                        const uint16_t* __restrict__ R,
+                                                        uint16_t* __restrict__ C, int M, int N, int K,
+                                                        int tiles_n, int n_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];
 
   const int tile = tile_of(blockIdx.x, n_tiles, tiles_n);
@@ -190,6 +197,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
 
   // ---- global load assignment
   // A tile: 256 rows x 8 chunks; thread t loads chunk (t & 7) of rows (t >> 3) + 64 i.
+  // W tile: thread t expands the 32-code group t & 1 of tile row t >> 1.
   // Rows past M (past N for W) are clamped: computed, never stored.
   const int ld_chunk = t & 7;
   const int ld_row = t >> 3;
@@ -197,16 +205,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
   const uint16_t* a_base = A + ld_chunk * 8;
   int a_r0 = min(tm * BM + ld_row, a_last), a_r1 = min(tm * BM + ld_row + 64, a_last);
   int a_r2 = min(tm * BM + ld_row + 128, a_last), a_r3 = min(tm * BM + ld_row + 192, a_last);
-  const uint16_t* w_base = static_cast<const uint16_t*>(Wv) + ld_chunk * 8;
-  int w_r0 = min(w_row<EPI>(tn, ld_row, N), w_last), w_r1 = min(w_row<EPI>(tn, ld_row + 64, N), w_last);
-  int w_r2 = min(w_row<EPI>(tn, ld_row + 128, N), w_last), w_r3 = min(w_row<EPI>(tn, ld_row + 192, N), w_last);
-  const int q_row = t >> 1;  // int4: 256 rows x 2 groups of 32
+  const int q_row = t >> 1;
   const int q_half = t & 1;
   const int q_r = min(w_row<EPI>(tn, q_row, N), w_last);
-  const uint8_t* q_src = static_cast<const uint8_t*>(Wv) + int64_t(q_r) * (K / 2) + q_half * 16;
+  const uint8_t* q_src = Wq + int64_t(q_r) * (K / 2) + q_half * 16;
   const uint16_t* s_src = Ws + int64_t(q_r) * (K / 32) + q_half;
 
-  uint4 ra0, ra1, ra2, ra3, rw0, rw1, rw2, rw3, rq;
+  uint4 ra0, ra1, ra2, ra3, rq;
   uint16_t rs = 0;
 
 #define BI_LOAD_GLOBAL(kt)                                                                  \
@@ -216,15 +221,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
     ra1 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r1) * K + ko);                 \
     ra2 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r2) * K + ko);                 \
     ra3 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r3) * K + ko);                 \
-    if constexpr (!W4) {                                                                    \
-      rw0 = *reinterpret_cast<const uint4*>(w_base + int64_t(w_r0) * K + ko);               \
-      rw1 = *reinterpret_cast<const uint4*>(w_base + int64_t(w_r1) * K + ko);               \
-      rw2 = *reinterpret_cast<const uint4*>(w_base + int64_t(w_r2) * K + ko);               \
-      rw3 = *reinterpret_cast<const uint4*>(w_base + int64_t(w_r3) * K + ko);               \
-    } else {                                                                                \
-      rq = *reinterpret_cast<const uint4*>(q_src + (kt) * (BK / 2));                        \
-      rs = s_src[(kt) * (BK / 32)];                                                         \
-    }                                                                                       \
+    rq = *reinterpret_cast<const uint4*>(q_src + (kt) * (BK / 2));                          \
+    rs = s_src[(kt) * (BK / 32)];                                                           \
   } while (0)
 
 #define BI_STORE_LDS(stage)                                                                 \
@@ -235,14 +233,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
     *reinterpret_cast<uint4*>(sA + lds_off(ld_row + 64, ld_chunk)) = ra1;                   \
     *reinterpret_cast<uint4*>(sA + lds_off(ld_row + 128, ld_chunk)) = ra2;                  \
     *reinterpret_cast<uint4*>(sA + lds_off(ld_row + 192, ld_chunk)) = ra3;                  \
-    if constexpr (!W4) {                                                                    \
-      *reinterpret_cast<uint4*>(sW + lds_off(ld_row, ld_chunk)) = rw0;                      \
-      *reinterpret_cast<uint4*>(sW + lds_off(ld_row + 64, ld_chunk)) = rw1;                 \
-      *reinterpret_cast<uint4*>(sW + lds_off(ld_row + 128, ld_chunk)) = rw2;                \
-      *reinterpret_cast<uint4*>(sW + lds_off(ld_row + 192, ld_chunk)) = rw3;                \
-    } else {                                                                                \
-      dequant_group_to_lds(rq, rs, sW, q_row, q_half);                                      \
-    }                                                                                       \
+    dequant_group_to_lds(rq, rs, sW, q_row, q_half);                                        \
   } while (0)
 
   f32x16 acc[4][2];
@@ -331,7 +322,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint16_t* __restrict_
   else if (nbm == 1) run(std::integral_constant<int, 1>{});
   else run(std::integral_constant<int, 0>{});
 
-  store_tile<EPI>(acc, C, R, M, N, tm, tn, wm, wn, lane);
+  store_tile<EPI, BN>(acc, C, R, M, N, tm, tn, wm, wn, lane);
 #undef BI_LOAD_GLOBAL
 #undef BI_STORE_LDS
 }
@@ -345,18 +336,30 @@ constexpr unsigned kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
 // itself, exactly where it needs them, so later loads stay in flight across barriers.
 __device__ __forceinline__ void ping_pong_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// bf16 GEMM, ping-pong schedule (see the file comment).  Offsets into A and W are
-// 32-bit byte offsets (the caller checks M K 2 and N K 2 < 2^32).
-template <int EPI>
+// One 16-byte-per-lane direct load into LDS: lane l's 16 bytes from src land at dst + 16 l
+// bytes (dst wave-uniform).  A plain function, so that calls from templates whose
+// arguments depend on template parameters are checked once, for the device only.
+__device__ __forceinline__ void load_lds_b128(const char* src, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+}
+
+// bf16 GEMM, ping-pong schedule (see the file comment), BM x BNT x BK tiles (BNT = 256, or
+// 192 for narrow weights).  Operand offsets are 32-bit byte offsets from the tile's first
+// row of A and of W (the caller checks (BM + 1) K 2 < 2^32, and for the gated form
+// (F + 256) K 2 < 2^32).
+template <int EPI, int BNT>
 __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ W,
                                                         const uint16_t* __restrict__ R,
                                                         uint16_t* __restrict__ C, int M, int N, int K,
                                                         int tiles_n, int n_tiles) {
+  static_assert(BNT == 256 || (BNT == 192 && EPI != kEpiGated), "tile width");
+  constexpr int NB = BNT / 64;        // 32-column blocks per wave (two waves along N)
+  constexpr int WB = BNT / 64;        // 1 KB blocks of the W tile each wave loads
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sW0[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t sW1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW0[BNT * BK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW1[BNT * BK];
 
   const int tile = tile_of(blockIdx.x, n_tiles, tiles_n);
   const int tm = tile / tiles_n;
@@ -367,34 +370,45 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
   const int wave = int(__builtin_amdgcn_readfirstlane(t >> 6));
   const int gp = wave >> 2;           // wave group; wave w runs on SIMD w % 4
   const int s4 = wave & 3;
-  const int wn = s4 & 1;              // 128 output columns
+  const int wn = s4 & 1;              // BNT / 2 output columns
   const int wm = (s4 >> 1) + 2 * gp;  // 64 output rows
 
-  // Direct loads: wave w fills 1 KB blocks 4w .. 4w + 3 (tile rows 32w .. 32w + 31) of
-  // each operand tile; lane l writes bytes 16 l of its block: tile row 8 b + l / 8,
-  // stored chunk l % 8, which holds logical chunk (l % 8) ^ ((row / 2) % 8) (the layout
-  // lds_off describes).  Rows past M (past N) are clamped: computed, never stored.
-  const int a_last = M - 1, w_last = (EPI == kEpiGated ? 2 * N : N) - 1;
-  uint32_t a_vo[4], w_vo[4];
+  // Direct loads: wave w fills 1 KB blocks 4w .. 4w + 3 of the A tile (rows 32w .. 32w +
+  // 31) and blocks WB w .. WB w + WB - 1 of the W tile; lane l writes bytes 16 l of its
+  // block: tile row 8 b + l / 8, stored chunk l % 8, which holds logical chunk
+  // (l % 8) ^ ((row / 2) % 8) (the layout lds_off describes).  Rows past M (past N) are
+  // clamped: computed, never stored.
+  const uint16_t* At = A + int64_t(tm) * BM * K;
+  const int w_first = EPI == kEpiGated ? tn * 128 : tn * BNT;
+  const uint16_t* Wt = W + int64_t(w_first) * K;
+  const int a_rows = min(BM, M - tm * BM);
+  const int w_last = (EPI == kEpiGated ? 2 * N : N) - 1;
+  uint32_t a_vo[4], w_vo[WB];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 32 * wave + 8 * j + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-    a_vo[j] = uint32_t(min(tm * BM + row, a_last)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
-    w_vo[j] = uint32_t(min(w_row<EPI>(tn, row, N), w_last)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
+    a_vo[j] = uint32_t(min(row, a_rows - 1)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
+  }
+#pragma unroll
+  for (int j = 0; j < WB; ++j) {
+    const int row = 8 * WB * wave + 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    w_vo[j] = uint32_t(min(w_row<EPI, BNT>(tn, row, N), w_last) - w_first) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
   }
   auto issue_loads = [&](int kt, uint16_t* dA, uint16_t* dW) {
-    const char* Ab = reinterpret_cast<const char*>(A + kt * BK);
-    const char* Wb = reinterpret_cast<const char*>(W + kt * BK);
+    const char* Ab = reinterpret_cast<const char*>(At + kt * BK);
+    const char* Wb = reinterpret_cast<const char*>(Wt + kt * BK);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(Ab + a_vo[j], dA + (4 * wave + j) * 512, 16, 0, 0);
+    for (int j = 0; j < 4; ++j) load_lds_b128(Ab + a_vo[j], dA + (4 * wave + j) * 512);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(Wb + w_vo[j], dW + (4 * wave + j) * 512, 16, 0, 0);
+    for (int j = 0; j < WB; ++j)
+      load_lds_b128(Wb + w_vo[j], dW + (WB * wave + j) * 512);
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[NB][2];
 #pragma unroll
-  for (int bn = 0; bn < 4; ++bn)
+  for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
     for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
@@ -404,8 +418,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
   // ((lane & 31) / 2) % 8: a fragment's LDS offset is (row base) * BK + a lane offset
   const int fr = lane & 31, fc = lane >> 5;
   const int fkey = (fr >> 1) & 7;
-  const int a_base = (wm * 64) * BK, w_base = (wn * 128) * BK;
-  bf16x8 wf[2][4], af[2][2];
+  const int a_base = (wm * 64) * BK, w_base = (wn * (BNT / 2)) * BK;
+  bf16x8 wf[2][NB], af[2][2];
   auto read_frags = [&](const uint16_t* sA, const uint16_t* sW, int h) {  // k-substeps 2h, 2h + 1
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
@@ -413,7 +427,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
 #pragma unroll
       for (int bm = 0; bm < 2; ++bm) af[k2][bm] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo + bm * 32 * BK);
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn) wf[k2][bn] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo + bn * 32 * BK);
+      for (int bn = 0; bn < NB; ++bn) wf[k2][bn] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo + bn * 32 * BK);
     }
   };
   // 32-row blocks entirely past M are skipped (padding work only)
@@ -425,7 +439,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
+      for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
         for (int bm = 0; bm < NBM; ++bm)
           acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[k2][bn], af[k2][bm], acc[bn][bm], 0, 0, 0);
@@ -468,32 +482,30 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
   else if (nbm == 1) run(std::integral_constant<int, 1>{});
   else run(std::integral_constant<int, 0>{});
 
-  store_tile<EPI>(acc, C, R, M, N, tm, tn, wm, wn, lane);
+  store_tile<EPI, BNT>(acc, C, R, M, N, tm, tn, wm, wn, lane);
 }
 
 }  // namespace
 
+// Column-tile width of the bf16 GEMM for a weight of N rows: 256, or 192 for weights of at
+// most kGemmNarrowN rows (not the gated form).  It depends on the weight alone, never on M.
+int gemm_tile_n(int64_t N, int epi) { return (epi != kEpiGated && N <= kGemmNarrowN) ? kGemmBNNarrow : BN; }
+
 // epi: kEpiPlain / kEpiResid (R [M, N]) / kEpiGated (N = F outputs, W [2F, K], F % 128 == 0)
 hipError_t launch_gemm_ex(const uint16_t* A, const uint16_t* W, const uint16_t* R, uint16_t* C, int64_t M,
                           int64_t N, int64_t K, int epi, hipStream_t s) {
+  const int bnt = gemm_tile_n(N, epi);
   const int tiles_m = int((M + BM - 1) / BM);
-  const int tiles_n = epi == kEpiGated ? int(N / 128) : int((N + BN - 1) / BN);
+  const int tiles_n = epi == kEpiGated ? int(N / 128) : int((N + bnt - 1) / bnt);
   const int n_tiles = tiles_m * tiles_n;
-  const int64_t w_rows = epi == kEpiGated ? 2 * N : N;
-  const bool pp = M * K * 2 < (int64_t(1) << 32) && w_rows * K * 2 < (int64_t(1) << 32);
-  const void* Wv = static_cast<const void*>(W);
-  const uint16_t* none = nullptr;
-#define BI_GEMM(E)                                                                                                   \
-  if (epi == E) {                                                                                                    \
-    if (pp)                                                                                                          \
-      hipLaunchKernelGGL(gemm_pp_kernel<E>, dim3(n_tiles), dim3(NT), 0, s, A, W, R, C, int(M), int(N), int(K),      \
-                         tiles_n, n_tiles);                                                                          \
-    else /* operands of 4 GiB or more: the register-staged schedule (64-bit addressing) */                         \
-      hipLaunchKernelGGL((gemm_kernel<false, E>), dim3(n_tiles), dim3(NT), 0, s, A, Wv, none, R, C, int(M), int(N), \
-                         int(K), tiles_n, n_tiles);                                                                  \
-    return hipGetLastError();                                                                                        \
+#define BI_GEMM(E, T)                                                                                          \
+  if (epi == E && bnt == T) {                                                                                  \
+    hipLaunchKernelGGL((gemm_pp_kernel<E, T>), dim3(n_tiles), dim3(NT), 0, s, A, W, R, C, int(M), int(N), int(K), \
+                       tiles_n, n_tiles);                                                                      \
+    return hipGetLastError();                                                                                  \
   }
-  BI_GEMM(kEpiPlain) BI_GEMM(kEpiResid) BI_GEMM(kEpiGated)
+  BI_GEMM(kEpiPlain, BN) BI_GEMM(kEpiResid, BN) BI_GEMM(kEpiGated, BN)
+  BI_GEMM(kEpiPlain, kGemmBNNarrow) BI_GEMM(kEpiResid, kGemmBNNarrow)
 #undef BI_GEMM
   return hipErrorInvalidValue;
 }
@@ -503,12 +515,11 @@ hipError_t launch_gemm_w4_ex(const uint8_t* Wq, const uint16_t* Ws, const uint16
   const int tiles_m = int((M + BM - 1) / BM);
   const int tiles_n = epi == kEpiGated ? int(N / 128) : int((N + BN - 1) / BN);
   const int n_tiles = tiles_m * tiles_n;
-  const void* Wv = static_cast<const void*>(Wq);
-#define BI_GEMM(E)                                                                                                 \
-  if (epi == E) {                                                                                                  \
-    hipLaunchKernelGGL((gemm_kernel<true, E>), dim3(n_tiles), dim3(NT), 0, s, A, Wv, Ws, R, C, int(M), int(N),    \
-                       int(K), tiles_n, n_tiles);                                                                  \
-    return hipGetLastError();                                                                                      \
+#define BI_GEMM(E)                                                                                               \
+  if (epi == E) {                                                                                                \
+    hipLaunchKernelGGL(gemm_w4_kernel<E>, dim3(n_tiles), dim3(NT), 0, s, A, Wq, Ws, R, C, int(M), int(N), int(K), \
+                       tiles_n, n_tiles);                                                                        \
+    return hipGetLastError();                                                                                    \
   }
   BI_GEMM(kEpiPlain) BI_GEMM(kEpiResid) BI_GEMM(kEpiGated)
 #undef BI_GEMM
@@ -526,4 +537,5 @@ hipError_t launch_gemm_w4(const uint16_t* A, const uint8_t* Wq, const uint16_t* 
 }
 
 }  // namespace bi
+
 

@@ -38,6 +38,9 @@ def test_library_exports_every_declared_function():
 def test_constants_and_build_id():
     assert bi.kv_split_size() == 256
     assert bi.gemm_tile() == (256, 256, 64)
+    # narrow bf16 weights get 192-wide column tiles; int4 weights and wide ones 256
+    assert [bi.gemm_tile_cols(n) for n in (8, 768, 2560, 3072, 3080, 4096, 24576)] == [192] * 4 + [256] * 3
+    assert bi.gemm_tile_cols(2560, int4_weights=True) == 256 and bi.gemm_tile_cols(0) == 0
     bid = bi.build_id()
     assert re.fullmatch(r"[0-9a-f]{16}", bid)
     for code in range(7):
@@ -62,6 +65,7 @@ def test_gemm_checks():
     assert L.bi_gemm(P16, P16b, P16c, 0, 8, 64, NUL) == SHAPE
     assert L.bi_gemm(P16, P16b, P16c, 1, 12, 64, NUL) == UNSUP     # N % 8
     assert L.bi_gemm(P16, P16b, P16c, 1, 8, 96, NUL) == UNSUP      # K % 64
+    assert L.bi_gemm(P16, P16b, P16c, 1, 8, (1 << 22) + 64, NUL) == UNSUP  # K above 2^22
     assert L.bi_gemm(MIS, P16b, P16c, 1, 8, 64, NUL) == ALIGN
     assert L.bi_gemm_w4(P16, P16b, NUL, P16c, 1, 8, 64, NUL) == NULL
     assert L.bi_gemm_w4(P16, P16b, ctypes.c_void_p(0x400001), P16c, 1, 8, 64, NUL) == ALIGN
@@ -86,6 +90,8 @@ def test_fused_gemm_checks():
     assert L.bi_gemm_swiglu(P16, P16b, P16c, 1, 120, 64, NUL) == UNSUP
     assert L.bi_gemm_swiglu(P16, P16b, P16c, 1, 128, 96, NUL) == UNSUP
     assert L.bi_gemm_swiglu(P16, P16b, MIS, 1, 128, 64, NUL) == ALIGN
+    # bf16 gated form: (F + 128) K 2 must stay below 2^32 (32-bit operand offsets)
+    assert L.bi_gemm_swiglu(P16, P16b, P16c, 1, 4096, 1 << 19, NUL) == UNSUP
     assert L.bi_gemm_w4_swiglu(P16, P16b, NUL, P16c, 1, 128, 64, NUL) == NULL
     assert L.bi_gemm_w4_swiglu(P16, P16b, P4, P16c, 1, 64, 64, NUL) == UNSUP
     assert L.bi_gemm_w4_swiglu(P16, P16b, ctypes.c_void_p(0x500001), P16c, 1, 128, 64, NUL) == ALIGN
