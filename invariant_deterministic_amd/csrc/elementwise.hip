@@ -9,9 +9,8 @@
 namespace bi {
 namespace {
 
-__global__ __launch_bounds__(256) void add_kernel(const uint4* __restrict__ x,
-                                                  const uint4* __restrict__ o,
-                                                  uint4* __restrict__ h, int64_t chunks) {
+// h may alias x or o (each thread reads its chunk of both before writing it): no __restrict__
+__global__ __launch_bounds__(256) void add_kernel(const uint4* x, const uint4* o, uint4* h, int64_t chunks) {
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < chunks;
        i += int64_t(gridDim.x) * 256) {
     float a[8], b[8];

@@ -127,8 +127,8 @@ __device__ __forceinline__ int w_row(int tn, int t, int F) {
 // 8*(r/4) + 4*(lane/32) + r%4) of a BM x BNT tile; C has N columns (the gated form: N = F
 // outputs, BNT = 256)
 template <int EPI, int BNT>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BNT / 64][2], uint16_t* __restrict__ C,
-                                           const uint16_t* __restrict__ R, int M, int N, int tm, int tn,
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BNT / 64][2], uint16_t* C,
+                                           const uint16_t* R, int M, int N, int tm, int tn,
                                            int wm, int wn, int lane) {
   static_assert(EPI != kEpiGated || BNT == 256, "the gated epilogue pairs 128-column halves of a 256 tile");
 #pragma unroll
@@ -180,8 +180,8 @@ template <int EPI>
 __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restrict__ A,
                                                         const uint8_t* __restrict__ Wq,
                                                         const uint16_t* __restrict__ Ws,
-                                                        const uint16_t* __restrict__ R,
-                                                        uint16_t* __restrict__ C, int M, int N, int K,
+                                                        const uint16_t* R,  // may alias C (resid)
+                                                        uint16_t* C, int M, int N, int K,
                                                         int tiles_n, int n_tiles) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];
 
@@ -350,8 +350,8 @@ __device__ __forceinline__ void load_lds_b128(const char* src, uint16_t* dst) {
 template <int EPI, int BNT>
 __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ W,
-                                                        const uint16_t* __restrict__ R,
-                                                        uint16_t* __restrict__ C, int M, int N, int K,
+                                                        const uint16_t* R,  // may alias C (resid)
+                                                        uint16_t* C, int M, int N, int K,
                                                         int tiles_n, int n_tiles) {
   static_assert(BNT == 256 || (BNT == 192 && EPI != kEpiGated), "tile width");
   constexpr int NB = BNT / 64;        // 32-column blocks per wave (two waves along N)
