@@ -160,6 +160,26 @@ def test_prefill_parity(T, q_start, hq, hkv, d):
         assert_bitwise(o[0].reshape(hq, d), np.repeat(v[0], g, axis=0), "prefill t=0 gives v0")
 
 
+
+def test_prefill_long_context():
+    """A short chunk at the end of a 30000-token context: parity on every row, and the same
+    bits when the chunk itself is split (the key blocks are aligned to position 0)."""
+    device()
+    hq, hkv, d = 32, 8, 128
+    q_start, T = 30000, 100
+    q = synth.normal_bf16(5300, (T, hq * d))
+    kd = synth.normal_bf16_device(5301, (q_start + T, hkv, d))
+    vd = synth.normal_bf16_device(5302, (q_start + T, hkv, d))
+    sc = np.float32(1 / math.sqrt(d))
+    announce("prefill long context", q_start, T)
+    qd = dev(q)
+    o = bits(bi.attn_prefill(qd, kd, vd, q_start, hq, hkv, d, float(sc)))
+    parts = [bits(bi.attn_prefill(qd[:37], kd, vd, q_start, hq, hkv, d, float(sc))),
+             bits(bi.attn_prefill(qd[37:], kd, vd, q_start + 37, hq, hkv, d, float(sc)))]
+    assert_bitwise(np.concatenate(parts), o, "prefill long context split 37 + 63")
+    ref = oracle.attention(q.reshape(T, hq, d), bits(kd), bits(vd), np.arange(q_start, q_start + T), sc)
+    assert_within_tolerance(o, ref.reshape(T, -1), f"prefill T={T} start={q_start}")
+
 @pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (4, 4, 64)])
 def test_prefill_chunk_invariance(hq, hkv, d):
     device()
