@@ -15,8 +15,9 @@
 //    v_mfma_f32_32x32x16_bf16 instructions in ascending order;
 //  * the MFMA unit treats every (row, column) slot of its 32 x 32 block the
 //    same way, so the bits of C[i, :] do not depend on which tile row or
-//    which slot row i lands in.
-// The tests check the last point empirically (every row at every position).
+//    which slot row i lands in, nor on the column-tile width.
+// The tests check the last point empirically (every row at every position, and
+// the 256-wide int4 GEMM against the 192-wide bf16 GEMM on the same weight).
 //
 // Int4 weights ("Residual nondeterminism" in the M-0002 limitations warns of
 // de-quantisation kernels with atomic additions): each thread expands one
@@ -57,7 +58,7 @@ namespace bi {
 namespace {
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int NT = 512;                 // 8 waves: 2 along N (128 each) x 4 along M (64 each)
+constexpr int NT = 512;                 // 8 waves: 2 along N (half the tile width each) x 4 along M (64 each)
 constexpr int TILE = BM * BK;           // bf16 elements of one operand tile (BM == BN)
 constexpr int kStoreAfter = 2;         // the next stage is written to LDS after this substep's MFMAs
 static_assert(BM == BN, "square tile assumed by the LDS layout");
