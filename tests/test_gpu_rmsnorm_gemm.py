@@ -218,3 +218,21 @@ def test_gemm_swiglu_equals_gemm_then_swiglu(m, f, k):
     if m > 1:
         one = bits(bi.gemm_w4_swiglu(a[m - 1:m], wq, ws))
         assert_bitwise(one[0], ref4[m - 1], "fused swiglu row alone")
+
+
+def test_gemm_operand_above_4gib():
+    """A of more than 4 GiB (2^21 + 77 rows of K = 1024): the kernel addresses operands from
+    each tile's first row, so rows past the 4 GiB mark are as correct as the first ones.
+    Sampled rows against the oracle, and bitwise against the same rows computed alone."""
+    device()
+    M, N, K = (1 << 21) + 77, 264, 1024
+    announce("gemm A above 4 GiB", M, N, K)
+    A = synth.normal_bf16_device(5400, (M, K))
+    assert A.numel() * 2 > (1 << 32)
+    w = synth.normal_bf16(5401, (N, K), 0.02)
+    C = bits(bi.gemm(A, dev(w)))
+    rows = np.array([0, 1, 255, 256, (1 << 20) + 3, (1 << 21) - 1, 1 << 21, M - 1])
+    a_rows = bits(A[torch.from_numpy(rows).cuda()])
+    del A
+    assert_within_tolerance(C[rows], oracle.gemm(a_rows, w), "gemm rows past 4 GiB")
+    assert_bitwise(C[rows], bits(bi.gemm(dev(a_rows), dev(w))), "rows alone")
