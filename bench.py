@@ -487,7 +487,7 @@ def run_copy(args, torch, bi, synth):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
