@@ -133,7 +133,10 @@ def mixed_workload(torch, bi, synth, B, prefill_order=False):
 
 
 def block_flops_bytes(H, F, hq, hkv, d, tokens, weight_bytes, prefill_T, decode_lens):
-    """Algorithmic work of one block step (roofline model)."""
+    """Algorithmic work of one block step and its roofline time: linear flops (all GEMMs),
+    causal prefill-attention flops (4 D per query-key pair per head), decode K/V bytes, and
+    T_roof = max(flops / MFMA peak, weight bytes / HBM) + prefill flops / MFMA peak +
+    (decode bytes + x, y and KV-append bytes) / HBM, intermediate activations at zero bytes."""
     lin = 2.0 * tokens * (H * (hq + 2 * hkv) * d + hq * d * H + H * 2 * F + F * H)
     pairs = prefill_T * (prefill_T + 1) / 2.0
     att_pf = 4.0 * d * hq * pairs
