@@ -443,13 +443,15 @@ template <int D, int G, bool Q8>
 hipError_t launch_t(const uint16_t* q, int64_t q_stride, const void* k, const void* v, const float* ks,
                     const float* vs, const int32_t* pages, uint16_t* o, int64_t o_stride, const PrefillSeq* seqs,
                     PrefillSeq single, int n_seqs, int max_tiles, int Hkv, float sscale, hipStream_t s) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
+  // compute units of the device, read once (a thread-safe constant): it only decides
+  // whether the grid is folded, never what a tile computes
+  static const int cus = [] {
+    int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      cus = 1;
-  }
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 1;
+    return n;
+  }();
   const int fold = int64_t(max_tiles) * Hkv * n_seqs > cus ? 1 : 0;
   const int gx = fold ? (max_tiles + 1) / 2 : max_tiles;
   hipLaunchKernelGGL((prefill_kernel<D, G, Q8>), dim3(gx, Hkv, n_seqs), dim3(NTH), 0, s, q, q_stride, k, v, ks, vs,
