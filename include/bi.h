@@ -367,7 +367,9 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
 
 /* Offsets (bytes into the block workspace) of every intermediate stage, for
  * inspection after a call: each is bf16 row-major [M, width].  Entries of a
- * stage the block does not have (no FFN) are SIZE_MAX.                      */
+ * stage the block does not store are SIZE_MAX: the FFN stages without an FFN,
+ * and o, d (always) and gu (when F % 128 == 0), which exist only inside the
+ * fused GEMM epilogues (bi_gemm[_w4]_residual / _swiglu).                   */
 typedef struct {
   size_t n1, qkv, q, attn, o, h, n2, gu, act, d;
   size_t decode_partials;
