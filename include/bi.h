@@ -90,7 +90,8 @@ int bi_gemm_tile_cols(int64_t N, int weight_format);
  * chosen from `hidden` alone.
  *   x     [rows, hidden] bf16      y [rows, hidden] bf16 (may not alias x)
  *   gamma [hidden] bf16
- *   rows >= 1; hidden % 8 == 0, 8 <= hidden <= 16384; eps finite, >= 0.     */
+ *   1 <= rows <= 2^26 - 1024; hidden % 8 == 0, 8 <= hidden <= 16384;
+ *   eps finite, >= 0.                                                        */
 bi_status bi_rmsnorm(const bi_bf16* x, const bi_bf16* gamma, bi_bf16* y,
                      int64_t rows, int64_t hidden, float eps, hipStream_t stream);
 
@@ -100,7 +101,8 @@ bi_status bi_rmsnorm(const bi_bf16* x, const bi_bf16* gamma, bi_bf16* y,
  * bi_gemm_tile_cols), no split-K: each C[i, j] is accumulated over
  * k = 0..K-1 in the same order for every M and every position of row i.
  *   A [M, K] bf16   W [N, K] bf16   C [M, N] bf16 (must not alias A or W)
- *   M >= 1; N >= 8, N % 8 == 0; K >= 64, K % 64 == 0, K <= 2^22.            */
+ *   M >= 1; N >= 8, N % 8 == 0; K >= 64, K % 64 == 0, K <= 2^22;
+ *   M K and M N at most 2^40; fewer than 2^23 tiles of 256 x 192.           */
 bi_status bi_gemm(const bi_bf16* A, const bi_bf16* W, bi_bf16* C,
                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
@@ -156,7 +158,7 @@ bi_status bi_swiglu(const bi_bf16* gu, bi_bf16* act, int64_t rows, int64_t F, hi
  * computed from the absolute position (so a prompt's keys do not depend on
  * how it was chunked: "Receipts", opening paragraph).  theta == 0 disables
  * the rotation (plain copy).
- *   pos [rows] int32 device, >= 0;  kv_row [rows] int64 device, row index
+ *   1 <= rows < 2^24;  pos [rows] int32 device, >= 0;  kv_row [rows] int64 device, row index
  *   into the pools k_pool, v_pool [*, Hkv, D] bf16.  D in {64, 128};
  *   Hq % Hkv == 0.  The pools' sizes are not passed: every kv_row[r] must
  *   name a row of the pools (bi_block_forward checks its rows against
@@ -175,7 +177,9 @@ bi_status bi_rope_kv(const bi_bf16* qkv, const int32_t* pos, const int64_t* kv_r
  * the prompt cache and run-ahead).
  *   q [T, Hq * D] bf16; k_cache, v_cache [>= q_start + T, Hkv, D] bf16 with
  *   keys 0 .. q_start + T - 1 valid; o [T, Hq * D] bf16.
- *   T >= 1, q_start >= 0; D in {64, 128}; Hq / Hkv in {1, 2, 4}.             */
+ *   T >= 1, q_start >= 0, q_start + T < 2^31, fewer than 2^23 query tiles
+ *   (a tile is 128 / (Hq / Hkv) positions); D in {64, 128};
+ *   Hq / Hkv in {1, 2, 4}; Hkv <= 65535.                                     */
 bi_status bi_attn_prefill(const bi_bf16* q, const bi_bf16* k_cache, const bi_bf16* v_cache,
                           bi_bf16* o, int64_t q_start, int64_t T,
                           int Hq, int Hkv, int D, float scale, hipStream_t stream);
@@ -238,7 +242,7 @@ bi_status bi_attn_decode_prefill_order(const bi_bf16* q, const bi_bf16* k_all, c
  * must name a page of the pools.  D in {64, 128}.                            */
 
 /* Quantise rows of bf16 keys and values [rows, Hkv, D] into pool rows
- * dst_row[r] (device int64 [rows]).                                          */
+ * dst_row[r] (device int64 [rows]); 1 <= rows < 2^26, Hkv <= 65535.          */
 bi_status bi_kv_append_q8(const bi_bf16* k, const bi_bf16* v, const int64_t* dst_row, int64_t rows,
                           int Hkv, int D, int8_t* k_pool, int8_t* v_pool, float* k_scale, float* v_scale,
                           hipStream_t stream);
@@ -317,6 +321,10 @@ bi_status bi_token_hash(const int32_t* ids, const int64_t* offsets, const int32_
  * attention.                                                                */
 typedef enum { BI_WEIGHTS_BF16 = 0, BI_WEIGHTS_INT4_G32 = 1 } bi_weight_format;
 typedef enum { BI_DECODE_SPLIT = 0, BI_DECODE_PREFILL_ORDER = 1 } bi_decode_order;
+/* KV cache of the block: contiguous bf16 rows per sequence, or the quantised,
+ * paged int8 cache of bi_kv_append_q8 ("Receipts", "What a receipt proves":
+ * a quantised cache is one of the load settings that decide the bits). */
+typedef enum { BI_KV_BF16 = 0, BI_KV_INT8_PAGED = 1 } bi_kv_format;
 
 typedef struct {
   int hidden;        /* H, % 8 == 0 */
@@ -329,6 +337,8 @@ typedef struct {
   int weight_format; /* bi_weight_format */
   int decode_order;  /* bi_decode_order: fixed 256-key split (default), or the
                         prefill kernel's key order (decoded bits = prefilled) */
+  int kv_format;     /* bi_kv_format; BI_KV_INT8_PAGED needs
+                        decode_order == BI_DECODE_PREFILL_ORDER */
 } bi_block_cfg;
 
 typedef struct {
@@ -348,13 +358,23 @@ typedef struct {
 typedef struct {
   int32_t q_len;   /* new tokens of this sequence in the step (>= 1) */
   int32_t ctx_len; /* tokens already in its cache (>= 0) */
-  int64_t kv_base; /* pool row holding its position 0 */
+  int64_t kv_base; /* bf16 pools: pool row holding its position 0; paged int8
+                      pools: first entry of the sequence's pages in
+                      bi_kv_pool.page_table (position p lives in pool row
+                      page_table[kv_base + p / 64] * 64 + p % 64) */
 } bi_seq;
 
 typedef struct {
-  bi_bf16* k;       /* [rows, Hkv, D] */
-  bi_bf16* v;       /* [rows, Hkv, D] */
-  int64_t rows;     /* capacity of the pools in token rows */
+  void* k;                   /* bf16 [rows, Hkv, D]; paged int8: codes [rows, Hkv, D] */
+  void* v;                   /* as k */
+  int64_t rows;              /* capacity of the pools in token rows (paged: pages * 64) */
+  float* k_scale;            /* paged int8 only: fp32 [rows, Hkv]; NULL for bf16 */
+  float* v_scale;            /* paged int8 only: fp32 [rows, Hkv]; NULL for bf16 */
+  const int32_t* page_table; /* paged int8 only: device int32 page indices, every one
+                                in 0 .. rows / 64 - 1 (an index outside is clamped
+                                into the pool when read and skipped when written:
+                                memory stays in bounds, results are then undefined) */
+  int64_t page_entries;      /* paged int8 only: entries in page_table */
 } bi_kv_pool;
 
 /* Step metadata.  The kernels read a packed device copy of the step
@@ -372,6 +392,8 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
  * fused GEMM epilogues (bi_gemm[_w4]_residual / _swiglu).                   */
 typedef struct {
   size_t n1, qkv, q, attn, o, h, n2, gu, act, d;
+  size_t kv_new;  /* paged int8 pools: the step's rotated keys, then its values,
+                     bf16 [2, M, Hkv, D] before quantisation; else SIZE_MAX */
   size_t decode_partials;
   size_t total;
 } bi_block_ws_layout;
@@ -384,7 +406,15 @@ bi_status bi_block_workspace(const bi_block_cfg* cfg, const bi_seq* seqs, int n_
  *     q_len).  d_meta: device copy of bi_step_pack(seqs) output.
  *   kv: pools updated in place at rows kv_base + ctx_len .. + q_len - 1;
  *     rows kv_base .. kv_base + ctx_len - 1 must hold the cached keys/values.
- *   x, y [M, H] bf16 (y may not alias x).  ws: >= layout.total bytes.       */
+ *     Paged int8 pools (cfg.kv_format): the step's keys and values are
+ *     quantised (bi_kv_append_q8) into positions ctx_len .. + q_len - 1 of
+ *     each sequence's pages, and attention reads bf16(code * scale) through
+ *     the page table (bi_attn_prefill_paged_q8, bi_attn_decode_paged_q8):
+ *     kv_base + ceil((ctx_len + q_len) / 64) <= page_entries.
+ *   x, y [M, H] bf16 (y may not alias x).  ws: >= layout.total bytes.
+ *   Limits (BI_ERR_UNSUPPORTED, checked before the first launch): M < 2^24;
+ *   at most 65535 decode and 65535 prefill sequences; decode lengths up to
+ *   2^30 keys; every GEMM within bi_gemm's limits.                          */
 bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w,
                            const bi_seq* seqs, int n_seqs, const void* d_meta,
                            const bi_kv_pool* kv, const bi_bf16* x, bi_bf16* y,

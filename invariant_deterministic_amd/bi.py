@@ -36,7 +36,7 @@ class BiError(RuntimeError):
 class bi_block_cfg(ctypes.Structure):
     _fields_ = [("hidden", c_int), ("n_q_heads", c_int), ("n_kv_heads", c_int), ("head_dim", c_int),
                 ("ffn", c_int), ("eps", c_float), ("rope_theta", c_double), ("weight_format", c_int),
-                ("decode_order", c_int)]
+                ("decode_order", c_int), ("kv_format", c_int)]
 
 
 class bi_weight(ctypes.Structure):
@@ -53,7 +53,8 @@ class bi_seq(ctypes.Structure):
 
 
 class bi_kv_pool(ctypes.Structure):
-    _fields_ = [("k", c_void_p), ("v", c_void_p), ("rows", c_int64)]
+    _fields_ = [("k", c_void_p), ("v", c_void_p), ("rows", c_int64), ("k_scale", c_void_p), ("v_scale", c_void_p),
+                ("page_table", c_void_p), ("page_entries", c_int64)]
 
 
 class bi_sampling(ctypes.Structure):
@@ -62,7 +63,7 @@ class bi_sampling(ctypes.Structure):
 
 
 class bi_block_ws_layout(ctypes.Structure):
-    _fields_ = [(n, c_size_t) for n in ("n1", "qkv", "q", "attn", "o", "h", "n2", "gu", "act", "d",
+    _fields_ = [(n, c_size_t) for n in ("n1", "qkv", "q", "attn", "o", "h", "n2", "gu", "act", "d", "kv_new",
                                         "decode_partials", "total")]
 
 
@@ -346,17 +347,20 @@ def attn_decode_prefill_order(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq
 
 
 class KvPoolQ8:
-    """An int8 paged KV pool: codes [rows, Hkv, D] and float32 scales [rows, Hkv] for K and V."""
+    """An int8 paged KV pool: codes [rows, Hkv, D] and float32 scales [rows, Hkv] for K and V.
+    For the block, ``page_table`` (device int32) lists page indices; a sequence's bi_seq
+    kv_base is the index of its first entry there."""
 
     PAGE = 64
 
-    def __init__(self, pages, Hkv, D, device="cuda"):
+    def __init__(self, pages, Hkv, D, device="cuda", page_table=None):
         rows = pages * self.PAGE
-        self.Hkv, self.D = Hkv, D
+        self.pages, self.Hkv, self.D = pages, Hkv, D
         self.k = torch.zeros((rows, Hkv, D), dtype=torch.int8, device=device)
         self.v = torch.zeros_like(self.k)
         self.ks = torch.zeros((rows, Hkv), dtype=torch.float32, device=device)
         self.vs = torch.zeros_like(self.ks)
+        self.page_table = page_table
 
 
 def kv_append_q8(pool, k, v, dst_row):
@@ -426,12 +430,13 @@ class BlockConfig:
     rope_theta: float = 0.0
     int4: bool = False
     decode_prefill_order: bool = False  # decode in the prefill kernel's key order
+    kv_q8: bool = False                 # paged int8 KV cache (needs decode_prefill_order)
 
     def c(self):
         return bi_block_cfg(self.hidden, self.n_q_heads, self.n_kv_heads, self.head_dim, self.ffn,
                             self.eps, float(self.rope_theta),
                             BI_WEIGHTS_INT4_G32 if self.int4 else BI_WEIGHTS_BF16,
-                            1 if self.decode_prefill_order else 0)
+                            1 if self.decode_prefill_order else 0, 1 if self.kv_q8 else 0)
 
 
 def _seq_array(seqs):
@@ -484,18 +489,86 @@ class Block:
                 setattr(w, field, bi_weight(val.data_ptr(), None))
         self._w = w
 
-    def forward(self, x, seqs, k_pool, v_pool, y=None, ws=None, meta=None):
-        """Run one step.  Returns (y, ws, layout); ws holds every intermediate stage."""
-        _dev(x, BF16, "x")
+    def check_args(self, x, seqs, k_pool, v_pool, y=None, ws=None, meta=None):
+        """Shape, dtype and device checks of forward()'s tensors, all before any launch: the
+        library sees raw pointers only, so a short x or a pool of another head layout would
+        otherwise be read and written out of bounds on the device."""
+        c = self.cfg
+        if not seqs:
+            raise ValueError("seqs: at least one sequence")
+        M = sum(int(s["q_len"]) for s in seqs)
+        pools = () if c.kv_q8 else (("k_pool", k_pool), ("v_pool", v_pool))
+        for name, t in (("x", x), *pools, ("y", y), ("ws", ws), ("meta", meta)):
+            if t is not None and not isinstance(t, torch.Tensor):
+                raise TypeError(f"{name}: expected a torch.Tensor")
+        if tuple(x.shape) != (M, c.hidden):
+            raise ValueError(f"x: shape {tuple(x.shape)}, expected (sum of q_len = {M}, hidden = {c.hidden})")
+        if y is not None and tuple(y.shape) != tuple(x.shape):
+            raise ValueError(f"y: shape {tuple(y.shape)}, expected {tuple(x.shape)}")
+        kv = (c.n_kv_heads, c.head_dim)
+        if c.kv_q8:
+            # paged int8 pool (KvPoolQ8 with a page table) in k_pool; v_pool unused
+            pool = k_pool
+            if not isinstance(pool, KvPoolQ8) or pool.page_table is None:
+                raise TypeError("k_pool: a KvPoolQ8 with a page_table for a paged int8 block")
+            if (pool.Hkv, pool.D) != kv:
+                raise ValueError(f"k_pool: heads {pool.Hkv} x {pool.D}, expected {kv[0]} x {kv[1]}")
+            pt = pool.page_table
+            if not isinstance(pt, torch.Tensor) or pt.dim() != 1:
+                raise ValueError("page_table: a 1-D int32 device tensor")
+            for s in seqs:
+                need = (int(s["ctx_len"]) + int(s["q_len"]) + KvPoolQ8.PAGE - 1) // KvPoolQ8.PAGE
+                if int(s["kv_base"]) + need > pt.shape[0]:
+                    raise ValueError(f"sequence {s} needs page-table entries past {pt.shape[0]}")
+            _dev(x, BF16, "x"); _dev(pool.k, torch.int8, "k codes"); _dev(pool.v, torch.int8, "v codes")
+            _dev(pool.ks, torch.float32, "k scales"); _dev(pool.vs, torch.float32, "v scales")
+            _dev(pt, torch.int32, "page_table")
+            k_pool, v_pool = pool.k, pool.v
+        else:
+            for name, p in (("k_pool", k_pool), ("v_pool", v_pool)):
+                if p.dim() != 3 or tuple(p.shape[1:]) != kv:
+                    raise ValueError(f"{name}: shape {tuple(p.shape)}, expected (rows, {kv[0]}, {kv[1]})")
+            if tuple(v_pool.shape) != tuple(k_pool.shape):
+                raise ValueError("k_pool and v_pool shapes differ")
+            for s in seqs:
+                if int(s["kv_base"]) + int(s["ctx_len"]) + int(s["q_len"]) > k_pool.shape[0]:
+                    raise ValueError(f"sequence {s} does not fit the pools' {k_pool.shape[0]} rows")
+            _dev(x, BF16, "x"); _dev(k_pool, BF16, "k_pool"); _dev(v_pool, BF16, "v_pool")
+        if y is not None:
+            _dev(y, BF16, "y")
+            if y.data_ptr() == x.data_ptr():
+                raise ValueError("y may not alias x")
+        if ws is not None:
+            _dev(ws, torch.uint8, "ws")
+        if meta is not None:
+            _dev(meta, torch.uint8, "meta")
+        for name, t in (("k_pool", k_pool), ("v_pool", v_pool), ("y", y), ("ws", ws), ("meta", meta)):
+            if t is not None and t.device != x.device:
+                raise ValueError(f"{name}: on {t.device}, x on {x.device}")
+        return M
+
+    def forward(self, x, seqs, k_pool, v_pool=None, y=None, ws=None, meta=None):
+        """Run one step.  Returns (y, ws, layout); ws holds every intermediate stage.
+        k_pool, v_pool: bf16 pools [rows, Hkv, D]; for a paged int8 block (cfg.kv_q8) a
+        KvPoolQ8 with its page table in k_pool and v_pool None."""
+        self.check_args(x, seqs, k_pool, v_pool, y, ws, meta)
         if meta is None:
             meta, arr = step_meta(seqs, x.device)
         else:
             arr = _seq_array(seqs)
+            need = lib().bi_step_meta_bytes(arr, len(seqs))
+            if need == 0 or meta.numel() < need:
+                raise ValueError(f"meta: {meta.numel()} bytes, the step needs {need}")
         lay = block_workspace(self.cfg, seqs)
         if ws is None or ws.numel() < lay.total:
             ws = torch.empty(max(lay.total, 256), dtype=torch.uint8, device=x.device)
         y = torch.empty_like(x) if y is None else y
-        pool = bi_kv_pool(k_pool.data_ptr(), v_pool.data_ptr(), k_pool.shape[0])
+        if self.cfg.kv_q8:
+            p = k_pool
+            pool = bi_kv_pool(p.k.data_ptr(), p.v.data_ptr(), p.k.shape[0], p.ks.data_ptr(), p.vs.data_ptr(),
+                              p.page_table.data_ptr(), p.page_table.shape[0])
+        else:
+            pool = bi_kv_pool(k_pool.data_ptr(), v_pool.data_ptr(), k_pool.shape[0], None, None, None, 0)
         _check(lib().bi_block_forward(ctypes.byref(self._c), ctypes.byref(self._w), arr, len(seqs),
                                       _ptr(meta), ctypes.byref(pool), _ptr(x), _ptr(y), _ptr(ws), ws.numel(),
                                       _stream()), "bi_block_forward")

@@ -32,27 +32,51 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 bi_status from_hip(hipError_t e) { return e == hipSuccess ? BI_OK : BI_ERR_HIP; }
 
+// Launch-grid limits: a grid dimension times its work-group size stays below 2^32
+// work-items, and the y / z dimensions below 65536.
+constexpr int64_t kMaxNormRows = (int64_t(1) << 26) - 1024;  // 64 work-items per row
+constexpr int64_t kMaxRopeRows = (int64_t(1) << 24) - 1;     // one 256-thread work-group per row
+constexpr int64_t kMaxQuantRows = (int64_t(1) << 26) - 1;    // one 64-thread work-group per (row, head, K|V)
+constexpr int64_t kMaxPrefillTiles = (int64_t(1) << 23) - 1; // 512-thread work-groups along x
+constexpr int64_t kMaxGridYZ = 65535;                        // decode requests, prefill sequences
+constexpr int64_t kMaxDecodeLen = int64_t(1) << 30;
+constexpr int64_t kMaxDecodeRuns = int64_t(1) << 24;         // split decode: one work-group per run and head
+constexpr int64_t kMaxGemmTiles = (int64_t(1) << 23) - 1;    // 512-thread work-groups along x
+
 bi_status check_rmsnorm(const void* x, const void* g, const void* y, int64_t rows, int64_t hidden,
                         float eps) {
   if (!x || !g || !y) return BI_ERR_NULL;
   if (rows < 1 || hidden < 1) return BI_ERR_SHAPE;
-  if (hidden % 8 || hidden > 16384 || rows > (int64_t(1) << 33)) return BI_ERR_UNSUPPORTED;
+  if (hidden % 8 || hidden > 16384 || rows > kMaxNormRows) return BI_ERR_UNSUPPORTED;
   if (!(eps >= 0.f) || eps > 3.0e38f) return BI_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(g) || !aligned16(y)) return BI_ERR_ALIGN;
   return BI_OK;
 }
 
-bi_status check_gemm(const void* A, const void* W, const void* C, int64_t M, int64_t N, int64_t K) {
-  if (!A || !W || !C) return BI_ERR_NULL;
+// Shape limits of the GEMM kernels (operand offsets, tile counts and the 1-D grid).
+bi_status gemm_shape(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 1) return BI_ERR_SHAPE;
   if (N % 8 || K % bi::kGemmBK) return BI_ERR_UNSUPPORTED;
   if (M > INT32_MAX || N > INT32_MAX || K > bi::kGemmMaxK || M * K > (int64_t(1) << 40) ||
       M * N > (int64_t(1) << 40))
     return BI_ERR_UNSUPPORTED;
   const int64_t tiles = ((M + bi::kGemmBM - 1) / bi::kGemmBM) * ((N + bi::kGemmBNNarrow - 1) / bi::kGemmBNNarrow);
-  if (tiles > INT32_MAX) return BI_ERR_UNSUPPORTED;
+  if (tiles > kMaxGemmTiles) return BI_ERR_UNSUPPORTED;
+  return BI_OK;
+}
+
+bi_status check_gemm(const void* A, const void* W, const void* C, int64_t M, int64_t N, int64_t K) {
+  if (!A || !W || !C) return BI_ERR_NULL;
+  const bi_status st = gemm_shape(M, N, K);
+  if (st != BI_OK) return st;
   if (!aligned16(A) || !aligned16(W) || !aligned16(C)) return BI_ERR_ALIGN;
   return BI_OK;
+}
+
+// Query tiles of a prefill chunk of T queries starting at q_start.
+int64_t prefill_tiles(int64_t q_start, int64_t T, int group) {
+  const int P = bi::prefill_positions_per_tile(group);
+  return (q_start + T - 1) / P - q_start / P + 1;
 }
 
 bool head_shape_ok(int Hq, int Hkv, int D, int max_group) {
@@ -137,8 +161,13 @@ bi_status check_cfg(const bi_block_cfg* c) {
     return BI_ERR_UNSUPPORTED;
   if (c->decode_order != BI_DECODE_SPLIT && c->decode_order != BI_DECODE_PREFILL_ORDER)
     return BI_ERR_UNSUPPORTED;
+  if (c->kv_format != BI_KV_BF16 && c->kv_format != BI_KV_INT8_PAGED) return BI_ERR_UNSUPPORTED;
+  // the paged int8 cache is read in the prefill kernel's key order only
+  if (c->kv_format == BI_KV_INT8_PAGED && c->decode_order != BI_DECODE_PREFILL_ORDER) return BI_ERR_UNSUPPORTED;
   return BI_OK;
 }
+
+bool paged(const bi_block_cfg& c) { return c.kv_format == BI_KV_INT8_PAGED; }
 
 bi_status check_weight(const bi_weight& w, int fmt) {
   if (!w.w) return BI_ERR_NULL;
@@ -188,6 +217,7 @@ WsLayout ws_layout(const bi_block_cfg& c, const StepSummary& s) {
   L.pub.gu = F && !ffn_fused(c) ? take(M * 2 * F * 2) : none;
   L.pub.act = F ? take(M * F * 2) : none;
   L.pub.d = none;
+  L.pub.kv_new = paged(c) ? take(2 * M * size_t(c.n_kv_heads) * c.head_dim * 2) : none;
   L.pub.decode_partials =
       s.n_decode && c.decode_order == BI_DECODE_SPLIT
           ? take(bi::decode_workspace_bytes(s.n_decode, s.max_decode_len, c.n_q_heads, c.head_dim))
@@ -330,7 +360,7 @@ bi_status bi_rope_kv(const bi_bf16* qkv, const int32_t* pos, const int64_t* kv_r
                      double theta, hipStream_t stream) {
   if (!qkv || !pos || !kv_row || !q_out || !k_pool || !v_pool) return BI_ERR_NULL;
   if (rows < 1) return BI_ERR_SHAPE;
-  if (rows > INT32_MAX) return BI_ERR_UNSUPPORTED;
+  if (rows > kMaxRopeRows) return BI_ERR_UNSUPPORTED;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
   if (D != 64 && D != 128) return BI_ERR_UNSUPPORTED;
   if (!(theta >= 0.0) || theta > 1e300) return BI_ERR_SHAPE;
@@ -352,15 +382,15 @@ bi_status bi_attn_prefill(const bi_bf16* q, const bi_bf16* k_cache, const bi_bf1
   if (!scale_ok(scale)) return BI_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o))
     return BI_ERR_ALIGN;
+  const int64_t tiles = prefill_tiles(q_start, T, Hq / Hkv);
+  if (tiles > kMaxPrefillTiles || Hkv > kMaxGridYZ) return BI_ERR_UNSUPPORTED;
   PrefillSeq one;
   one.q_row = 0;
   one.kv_base = 0;
   one.q_start = int32_t(q_start);
   one.q_len = int32_t(T);
-  const int P = bi::prefill_positions_per_tile(Hq / Hkv);
-  const int tiles = int((q_start + T - 1) / P - q_start / P + 1);
   return from_hip(bi::launch_attn_prefill(q, int64_t(Hq) * D, k_cache, v_cache, o, int64_t(Hq) * D,
-                                          nullptr, &one, 1, tiles, Hq, Hkv, D, scale, stream));
+                                          nullptr, &one, 1, int(tiles), Hq, Hkv, D, scale, stream));
 }
 
 size_t bi_attn_decode_workspace(int B, int64_t max_kv_len, int Hq, int D) {
@@ -374,12 +404,12 @@ bi_status bi_attn_decode(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* 
                          size_t ws_bytes, bi_bf16* o, hipStream_t stream) {
   if (!q || !k_all || !v_all || !kv_offset || !kv_len || !o) return BI_ERR_NULL;
   if (B < 1 || max_kv_len < 1) return BI_ERR_SHAPE;
-  if (B > 65535 || max_kv_len > (int64_t(1) << 30)) return BI_ERR_UNSUPPORTED;
+  if (B > kMaxGridYZ || max_kv_len > kMaxDecodeLen || Hkv > kMaxGridYZ) return BI_ERR_UNSUPPORTED;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
   if (!head_shape_ok(Hq, Hkv, D, 8)) return BI_ERR_UNSUPPORTED;
   if (!scale_ok(scale)) return BI_ERR_SHAPE;
   const int64_t run_keys = int64_t(bi::kKvSplit) * bi::kDecodeRun;
-  if (int64_t(B) * ((max_kv_len + run_keys - 1) / run_keys) > (int64_t(1) << 24)) return BI_ERR_UNSUPPORTED;
+  if (int64_t(B) * ((max_kv_len + run_keys - 1) / run_keys) > kMaxDecodeRuns) return BI_ERR_UNSUPPORTED;
   if (!ws) return BI_ERR_WORKSPACE;
   if (ws_bytes < bi::decode_workspace_bytes(B, max_kv_len, Hq, D)) return BI_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(k_all) || !aligned16(v_all) || !aligned16(o) || !aligned16(ws) ||
@@ -395,7 +425,7 @@ bi_status bi_attn_decode_prefill_order(const bi_bf16* q, const bi_bf16* k_all, c
                                        int Hkv, int D, float scale, bi_bf16* o, hipStream_t stream) {
   if (!q || !k_all || !v_all || !kv_offset || !kv_len || !o) return BI_ERR_NULL;
   if (B < 1 || max_kv_len < 1) return BI_ERR_SHAPE;
-  if (B > 65535 || max_kv_len > (int64_t(1) << 30)) return BI_ERR_UNSUPPORTED;
+  if (B > kMaxGridYZ || max_kv_len > kMaxDecodeLen || Hkv > kMaxGridYZ) return BI_ERR_UNSUPPORTED;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
   if (!head_shape_ok(Hq, Hkv, D, 8)) return BI_ERR_UNSUPPORTED;
   if (!scale_ok(scale)) return BI_ERR_SHAPE;
@@ -412,7 +442,7 @@ bi_status bi_kv_append_q8(const bi_bf16* k, const bi_bf16* v, const int64_t* dst
                           hipStream_t stream) {
   if (!k || !v || !dst_row || !k_pool || !v_pool || !k_scale || !v_scale) return BI_ERR_NULL;
   if (rows < 1 || Hkv < 1) return BI_ERR_SHAPE;
-  if (rows > INT32_MAX || Hkv > 65535 || (D != 64 && D != 128)) return BI_ERR_UNSUPPORTED;
+  if (rows > kMaxQuantRows || Hkv > kMaxGridYZ || (D != 64 && D != 128)) return BI_ERR_UNSUPPORTED;
   if (!aligned16(k) || !aligned16(v) || !aligned8(dst_row) || !aligned16(k_pool) || !aligned16(v_pool) ||
       (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u))
     return BI_ERR_ALIGN;
@@ -433,15 +463,16 @@ bi_status bi_attn_prefill_paged_q8(const bi_bf16* q, const int8_t* k_pool, const
       (reinterpret_cast<uintptr_t>(k_scale) & 3u) || (reinterpret_cast<uintptr_t>(v_scale) & 3u) ||
       (reinterpret_cast<uintptr_t>(block_table) & 3u))
     return BI_ERR_ALIGN;
+  const int64_t tiles = prefill_tiles(q_start, T, Hq / Hkv);
+  if (tiles > kMaxPrefillTiles || Hkv > kMaxGridYZ) return BI_ERR_UNSUPPORTED;
   PrefillSeq one;
   one.q_row = 0;
   one.kv_base = 0;
   one.q_start = int32_t(q_start);
   one.q_len = int32_t(T);
-  const int P = bi::prefill_positions_per_tile(Hq / Hkv);
-  const int tiles = int((q_start + T - 1) / P - q_start / P + 1);
-  return from_hip(bi::launch_attn_prefill_q8(q, int64_t(Hq) * D, k_pool, v_pool, k_scale, v_scale, block_table, o,
-                                             int64_t(Hq) * D, &one, tiles, Hq, Hkv, D, scale, stream));
+  return from_hip(bi::launch_attn_prefill_q8(q, int64_t(Hq) * D, k_pool, v_pool, k_scale, v_scale, block_table,
+                                             INT64_MAX, o, int64_t(Hq) * D, nullptr, &one, 1, int(tiles), Hq, Hkv, D,
+                                             scale, stream));
 }
 
 bi_status bi_attn_decode_paged_q8(const bi_bf16* q, const int8_t* k_pool, const int8_t* v_pool,
@@ -451,7 +482,7 @@ bi_status bi_attn_decode_paged_q8(const bi_bf16* q, const int8_t* k_pool, const 
                                   hipStream_t stream) {
   if (!q || !k_pool || !v_pool || !k_scale || !v_scale || !block_tables || !kv_len || !o) return BI_ERR_NULL;
   if (B < 1 || max_kv_len < 1 || max_pages < 1) return BI_ERR_SHAPE;
-  if (B > 65535 || max_kv_len > (int64_t(1) << 30)) return BI_ERR_UNSUPPORTED;
+  if (B > kMaxGridYZ || max_kv_len > kMaxDecodeLen || Hkv > kMaxGridYZ) return BI_ERR_UNSUPPORTED;
   if (int64_t(max_pages) * bi::kPrefillKeyBlock < max_kv_len) return BI_ERR_SHAPE;
   if (Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
   if (!head_shape_ok(Hq, Hkv, D, 8)) return BI_ERR_UNSUPPORTED;
@@ -461,8 +492,9 @@ bi_status bi_attn_decode_paged_q8(const bi_bf16* q, const int8_t* k_pool, const 
       (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(kv_len) & 3u) ||
       (reinterpret_cast<uintptr_t>(order) & 3u))
     return BI_ERR_ALIGN;
-  return from_hip(bi::launch_attn_decode_po_q8(q, k_pool, v_pool, k_scale, v_scale, block_tables, max_pages, kv_len,
-                                               order, B, max_kv_len, Hq, Hkv, D, scale, o, stream));
+  return from_hip(bi::launch_attn_decode_po_q8(q, int64_t(Hq) * D, k_pool, v_pool, k_scale, v_scale, block_tables,
+                                               max_pages, INT64_MAX, nullptr, kv_len, order, B, max_kv_len, Hq, Hkv,
+                                               D, scale, o, int64_t(Hq) * D, stream));
 }
 
 bi_status bi_sample(const bi_bf16* logits, int64_t rows, int64_t vocab, const bi_sampling* params,
@@ -522,6 +554,14 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
   if (n_runs > INT32_MAX) return BI_ERR_UNSUPPORTED;
   const MetaLayout L = meta_layout(n_seqs, s.M, n_runs);
   if (bytes < L.total) return BI_ERR_WORKSPACE;
+  // scratch for sorting the run list, allocated before the output is touched (no exception
+  // leaves this function)
+  std::vector<std::pair<int32_t, int32_t>> rl;
+  try {
+    rl.resize(static_cast<size_t>(n_runs));
+  } catch (...) {
+    return BI_ERR_UNSUPPORTED;
+  }
   memset(host_meta, 0, L.total);
   int64_t* hdr = at<int64_t>(host_meta, 0);
   hdr[0] = n_seqs;
@@ -567,7 +607,6 @@ bi_status bi_step_pack(const bi_seq* seqs, int n_seqs, void* host_meta, size_t b
   }
   // runs with the most units first (ties in list order): only the launch order
   {
-    std::vector<std::pair<int32_t, int32_t>> rl(static_cast<size_t>(n_runs));
     for (int64_t i = 0; i < n_runs; ++i) rl[size_t(i)] = {runs[2 * i], runs[2 * i + 1]};
     auto run_units = [&](const std::pair<int32_t, int32_t>& r) {
       return std::min<int64_t>(bi::kDecodeRun, units_of(dc[r.first].kv_len) - r.second);
@@ -619,8 +658,20 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
   }
   if (!kv->k || !kv->v) return BI_ERR_NULL;
   if (kv->rows < 1) return BI_ERR_SHAPE;
-  for (int i = 0; i < n_seqs; ++i)
-    if (seqs[i].kv_base + int64_t(seqs[i].ctx_len) + seqs[i].q_len > kv->rows) return BI_ERR_SHAPE;
+  const int64_t kb = bi::kPrefillKeyBlock;  // page size of the paged cache
+  if (paged(c)) {
+    if (!kv->k_scale || !kv->v_scale || !kv->page_table) return BI_ERR_NULL;
+    if (kv->rows % kb || kv->page_entries < 1) return BI_ERR_SHAPE;
+    for (int i = 0; i < n_seqs; ++i)
+      if (seqs[i].kv_base + (int64_t(seqs[i].ctx_len) + seqs[i].q_len + kb - 1) / kb > kv->page_entries)
+        return BI_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(kv->k_scale) & 3u) || (reinterpret_cast<uintptr_t>(kv->v_scale) & 3u) ||
+        (reinterpret_cast<uintptr_t>(kv->page_table) & 3u))
+      return BI_ERR_ALIGN;
+  } else {
+    for (int i = 0; i < n_seqs; ++i)
+      if (seqs[i].kv_base + int64_t(seqs[i].ctx_len) + seqs[i].q_len > kv->rows) return BI_ERR_SHAPE;
+  }
   if (x == y) return BI_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(y) || !aligned16(w->gamma1) || !aligned16(kv->k) ||
       !aligned16(kv->v) || !aligned16(d_meta) || !aligned16(ws))
@@ -632,7 +683,17 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
   const int H = c.hidden, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, F = c.ffn;
   const int qkv_n = (Hq + 2 * Hkv) * D;
   const int64_t n_runs = decode_runs(seqs, n_seqs);
-  if (n_runs > INT32_MAX) return BI_ERR_UNSUPPORTED;
+  // every launch below must fit its grid: checked here, before the first one is enqueued
+  if (M > kMaxRopeRows || M > kMaxNormRows) return BI_ERR_UNSUPPORTED;
+  if (s.n_decode > kMaxGridYZ || s.n_prefill > kMaxGridYZ || Hkv > kMaxGridYZ) return BI_ERR_UNSUPPORTED;
+  if (s.max_decode_len > kMaxDecodeLen || n_runs > kMaxDecodeRuns) return BI_ERR_UNSUPPORTED;
+  int64_t max_tiles = 0;
+  for (int i = 0; i < n_seqs; ++i)
+    if (seqs[i].q_len > 1)
+      max_tiles = std::max(max_tiles, prefill_tiles(seqs[i].ctx_len, seqs[i].q_len, Hq / Hkv));
+  if (max_tiles > kMaxPrefillTiles) return BI_ERR_UNSUPPORTED;
+  if ((st = gemm_shape(M, qkv_n, H)) != BI_OK || (st = gemm_shape(M, H, int64_t(Hq) * D)) != BI_OK) return st;
+  if (F && ((st = gemm_shape(M, 2 * int64_t(F), H)) != BI_OK || (st = gemm_shape(M, H, F)) != BI_OK)) return st;
   const MetaLayout ML = meta_layout(n_seqs, M, n_runs);
   uint16_t* n1 = at<uint16_t>(ws, L.pub.n1);
   uint16_t* qkv = at<uint16_t>(ws, L.pub.qkv);
@@ -648,32 +709,49 @@ bi_status bi_block_forward(const bi_block_cfg* cfg, const bi_block_weights* w, c
   } while (0)
   BI_TRY(bi::launch_rmsnorm(x, w->gamma1, n1, M, H, c.eps, stream));
   BI_TRY(run_gemm(c, w->qkv, n1, qkv, M, qkv_n, H, stream));
-  BI_TRY(bi::launch_rope_kv(qkv, at<int32_t>(d_meta, ML.pos), at<int64_t>(d_meta, ML.kv), q, kv->k,
-                            kv->v, M, Hq, Hkv, D, c.rope_theta, stream));
   const float scale = float(1.0 / __builtin_sqrt(double(D)));
-  if (s.n_prefill) {
-    int max_tiles = 0;
-    const int P = bi::prefill_positions_per_tile(Hq / Hkv);
-    for (int i = 0; i < n_seqs; ++i)
-      if (seqs[i].q_len > 1) {
-        const int first = seqs[i].ctx_len / P;
-        const int last = (seqs[i].ctx_len + seqs[i].q_len - 1) / P;
-        max_tiles = std::max(max_tiles, last - first + 1);
-      }
-    BI_TRY(bi::launch_attn_prefill(q, int64_t(Hq) * D, kv->k, kv->v, attn, int64_t(Hq) * D,
-                                   at<PrefillSeq>(d_meta, ML.prefill), nullptr, s.n_prefill,
-                                   max_tiles, Hq, Hkv, D, scale, stream));
-  }
-  if (s.n_decode && c.decode_order == BI_DECODE_PREFILL_ORDER) {
-    BI_TRY(bi::launch_attn_decode_po(q, int64_t(Hq) * D, kv->k, kv->v, at<DecodeSeq>(d_meta, ML.decode),
-                                     nullptr, nullptr, at<int32_t>(d_meta, ML.order), s.n_decode,
-                                     s.max_decode_len, Hq, Hkv, D, scale, attn, int64_t(Hq) * D, stream));
-  } else if (s.n_decode) {
-    BI_TRY(bi::launch_attn_decode(q, int64_t(Hq) * D, kv->k, kv->v, at<DecodeSeq>(d_meta, ML.decode),
-                                  at<int2>(d_meta, ML.runs), int(n_runs), s.n_decode,
-                                  s.max_decode_len, Hq, Hkv, D, scale,
-                                  at<void>(ws, L.pub.decode_partials), attn, int64_t(Hq) * D,
-                                  stream));
+  if (paged(c)) {
+    // rotated keys and the values go to the workspace (rows of the step), then into the
+    // sequences' pages as int8 codes and scales; attention reads the pages
+    uint16_t* k_new = at<uint16_t>(ws, L.pub.kv_new);
+    uint16_t* v_new = k_new + M * Hkv * D;
+    int8_t* kq = static_cast<int8_t*>(kv->k);
+    int8_t* vq = static_cast<int8_t*>(kv->v);
+    const int64_t n_pages = kv->rows / kb;
+    BI_TRY(bi::launch_rope_kv(qkv, at<int32_t>(d_meta, ML.pos), nullptr, q, k_new, v_new, M, Hq, Hkv, D,
+                              c.rope_theta, stream));
+    BI_TRY(bi::launch_kv_quant_paged(k_new, v_new, at<int64_t>(d_meta, ML.kv), at<int32_t>(d_meta, ML.pos),
+                                     kv->page_table, n_pages, M, Hkv, D, kq, vq, kv->k_scale, kv->v_scale, stream));
+    if (s.n_prefill)
+      BI_TRY(bi::launch_attn_prefill_q8(q, int64_t(Hq) * D, kq, vq, kv->k_scale, kv->v_scale, kv->page_table, n_pages,
+                                        attn, int64_t(Hq) * D, at<PrefillSeq>(d_meta, ML.prefill), nullptr,
+                                        s.n_prefill, int(max_tiles), Hq, Hkv, D, scale, stream));
+    if (s.n_decode)
+      BI_TRY(bi::launch_attn_decode_po_q8(q, int64_t(Hq) * D, kq, vq, kv->k_scale, kv->v_scale, kv->page_table, 0,
+                                          n_pages, at<DecodeSeq>(d_meta, ML.decode), nullptr,
+                                          at<int32_t>(d_meta, ML.order), s.n_decode, s.max_decode_len, Hq, Hkv, D,
+                                          scale, attn, int64_t(Hq) * D, stream));
+  } else {
+    uint16_t* kc = static_cast<uint16_t*>(kv->k);
+    uint16_t* vc = static_cast<uint16_t*>(kv->v);
+    BI_TRY(bi::launch_rope_kv(qkv, at<int32_t>(d_meta, ML.pos), at<int64_t>(d_meta, ML.kv), q, kc,
+                              vc, M, Hq, Hkv, D, c.rope_theta, stream));
+    if (s.n_prefill) {
+      BI_TRY(bi::launch_attn_prefill(q, int64_t(Hq) * D, kc, vc, attn, int64_t(Hq) * D,
+                                     at<PrefillSeq>(d_meta, ML.prefill), nullptr, s.n_prefill,
+                                     int(max_tiles), Hq, Hkv, D, scale, stream));
+    }
+    if (s.n_decode && c.decode_order == BI_DECODE_PREFILL_ORDER) {
+      BI_TRY(bi::launch_attn_decode_po(q, int64_t(Hq) * D, kc, vc, at<DecodeSeq>(d_meta, ML.decode),
+                                       nullptr, nullptr, at<int32_t>(d_meta, ML.order), s.n_decode,
+                                       s.max_decode_len, Hq, Hkv, D, scale, attn, int64_t(Hq) * D, stream));
+    } else if (s.n_decode) {
+      BI_TRY(bi::launch_attn_decode(q, int64_t(Hq) * D, kc, vc, at<DecodeSeq>(d_meta, ML.decode),
+                                    at<int2>(d_meta, ML.runs), int(n_runs), s.n_decode,
+                                    s.max_decode_len, Hq, Hkv, D, scale,
+                                    at<void>(ws, L.pub.decode_partials), attn, int64_t(Hq) * D,
+                                    stream));
+    }
   }
   BI_TRY(run_gemm(c, w->o, attn, h, M, H, int64_t(Hq) * D, stream, bi::kEpiResid, x));  // h = x + o
   if (F) {

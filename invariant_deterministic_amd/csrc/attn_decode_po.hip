@@ -49,7 +49,7 @@ template <int D, int G, bool Q8>
 __global__ __launch_bounds__(NT) void decode_po_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const void* __restrict__ k_all,
     const void* __restrict__ v_all, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-    const int32_t* __restrict__ block_tables, int max_pages, const DecodeSeq* __restrict__ seqs,
+    const int32_t* __restrict__ block_tables, int max_pages, int64_t n_pages, const DecodeSeq* __restrict__ seqs,
     const int64_t* __restrict__ kv_offset, const int32_t* __restrict__ kv_len,
     const int32_t* __restrict__ order, int Hkv, int64_t max_len, float sscale,
     uint16_t* __restrict__ o, int64_t o_stride) {
@@ -65,15 +65,20 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
 
   const int g = blockIdx.x;
   const int b = order ? order[blockIdx.y] : int(blockIdx.y);
-  int64_t qrow, koff, L;
+  // koff: cache row of key 0 (bf16); pt: first page-table entry of the request (int8 cache,
+  // addressed through page tables: the sequence's kv_offset in one flat table, or row b of
+  // per-request tables [B, max_pages])
+  int64_t qrow, koff, L, pt;
   if (seqs) {
     const DecodeSeq sq = seqs[b];
     qrow = sq.q_row;
-    koff = sq.kv_offset;
+    koff = Q8 ? 0 : sq.kv_offset;
+    pt = Q8 ? sq.kv_offset : 0;
     L = sq.kv_len;
   } else {
     qrow = b;
-    koff = Q8 ? 0 : kv_offset[b];  // the int8 cache is addressed through block tables
+    koff = Q8 ? 0 : kv_offset[b];
+    pt = int64_t(b) * max_pages;
     L = kv_len[b];
   }
   const int lane = threadIdx.x & 63;
@@ -119,13 +124,16 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
   // int8 paged cache: LD codes per key (NQ dwords) and the key's scale; block blk is page
   // block_tables[b][blk], rows page * 64 .. + 63 of the pool
   constexpr int NQ = LD / 4;
-  const int32_t* bt = block_tables + int64_t(b) * max_pages;
+  const int32_t* bt = block_tables + pt;
   const uint32_t qlane_off = uint32_t(grp) * uint32_t(row_stride) + uint32_t(l16) * LD;
   auto load_q = [&](uint32_t (&kd)[8][NQ], float& ks, uint32_t (&vd)[8][NQ], float& vs, int blk) {
     const int64_t first = int64_t(blk) * KB + 32 * kh;
     const int64_t left = L - first;
     const uint32_t nv = uint32_t(left <= 0 ? 0 : (left < 32 ? left : 32));
-    const int64_t prow = int64_t(bt[min(blk, nblk - 1)]) * KB + 32 * kh;  // past the keys: any real page, nothing read
+    // past the keys: any real page, nothing read; an index outside the pool is clamped into it
+    int64_t page = bt[min(blk, nblk - 1)];
+    page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
+    const int64_t prow = page * KB + 32 * kh;
     const int8_t* kb8 = static_cast<const int8_t*>(k_all) + prow * row_stride + g * D;
     const int8_t* vb8 = static_cast<const int8_t*>(v_all) + prow * row_stride + g * D;
     const __amdgpu_buffer_rsrc_t krs = buf_rsrc(wave_uniform(reinterpret_cast<const uint16_t*>(kb8)),
@@ -343,11 +351,11 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
 
 template <int D, int G, bool Q8>
 hipError_t launch_t(const uint16_t* q, int64_t q_stride, const void* k_all, const void* v_all, const float* ks,
-                    const float* vs, const int32_t* bt, int max_pages, const DecodeSeq* seqs, const int64_t* kv_offset,
-                    const int32_t* kv_len, const int32_t* order, int B, int64_t max_len, int Hkv, float sscale,
-                    uint16_t* o, int64_t o_stride, hipStream_t s) {
+                    const float* vs, const int32_t* bt, int max_pages, int64_t n_pages, const DecodeSeq* seqs,
+                    const int64_t* kv_offset, const int32_t* kv_len, const int32_t* order, int B, int64_t max_len,
+                    int Hkv, float sscale, uint16_t* o, int64_t o_stride, hipStream_t s) {
   hipLaunchKernelGGL((decode_po_kernel<D, G, Q8>), dim3(Hkv, B), dim3(NT), 0, s, q, q_stride, k_all, v_all, ks, vs, bt,
-                     max_pages, seqs, kv_offset, kv_len, order, Hkv, max_len, sscale, o, o_stride);
+                     max_pages, n_pages, seqs, kv_offset, kv_len, order, Hkv, max_len, sscale, o, o_stride);
   return hipGetLastError();
 }
 
@@ -362,26 +370,27 @@ hipError_t launch_attn_decode_po(const uint16_t* q, int64_t q_row_stride, const 
   const int G = Hq / Hkv;
 #define BI_DPO(DD, GG)                                                                                         \
   if (D == DD && G == GG)                                                                                    \
-    return launch_t<DD, GG, false>(q, q_row_stride, k_all, v_all, nullptr, nullptr, nullptr, 0, d_seqs, kv_offset, \
-                                   kv_len, d_order, B, max_kv_len, Hkv, sscale, o, o_row_stride, s);
+    return launch_t<DD, GG, false>(q, q_row_stride, k_all, v_all, nullptr, nullptr, nullptr, 0, 0, d_seqs,      \
+                                   kv_offset, kv_len, d_order, B, max_kv_len, Hkv, sscale, o, o_row_stride, s);
   BI_DPO(64, 1) BI_DPO(64, 2) BI_DPO(64, 4) BI_DPO(64, 8)
   BI_DPO(128, 1) BI_DPO(128, 2) BI_DPO(128, 4) BI_DPO(128, 8)
 #undef BI_DPO
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_decode_po_q8(const uint16_t* q, const int8_t* k_pool, const int8_t* v_pool,
-                                    const float* k_scale, const float* v_scale, const int32_t* block_tables,
-                                    int max_pages, const int32_t* kv_len, const int32_t* d_order, int B,
+hipError_t launch_attn_decode_po_q8(const uint16_t* q, int64_t q_row_stride, const int8_t* k_pool,
+                                    const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                                    const int32_t* block_tables, int max_pages, int64_t n_pages,
+                                    const DecodeSeq* d_seqs, const int32_t* kv_len, const int32_t* d_order, int B,
                                     int64_t max_kv_len, int Hq, int Hkv, int D, float scale, uint16_t* o,
-                                    hipStream_t s) {
+                                    int64_t o_row_stride, hipStream_t s) {
   const float sscale = scale * 1.4426950408889634f;
   const int G = Hq / Hkv;
-  const int64_t qs = int64_t(Hq) * D;
 #define BI_DPO(DD, GG)                                                                                          \
   if (D == DD && G == GG)                                                                                     \
-    return launch_t<DD, GG, true>(q, qs, k_pool, v_pool, k_scale, v_scale, block_tables, max_pages, nullptr,      \
-                                  nullptr, kv_len, d_order, B, max_kv_len, Hkv, sscale, o, qs, s);
+    return launch_t<DD, GG, true>(q, q_row_stride, k_pool, v_pool, k_scale, v_scale, block_tables, max_pages,     \
+                                  n_pages, d_seqs, nullptr, kv_len, d_order, B, max_kv_len, Hkv, sscale, o,      \
+                                  o_row_stride, s);
   BI_DPO(64, 1) BI_DPO(64, 2) BI_DPO(64, 4) BI_DPO(64, 8)
   BI_DPO(128, 1) BI_DPO(128, 2) BI_DPO(128, 4) BI_DPO(128, 8)
 #undef BI_DPO

@@ -100,7 +100,7 @@ template <int D, int G, bool Q8>
 __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-    const int32_t* __restrict__ pages, uint16_t* __restrict__ o, int64_t o_stride,
+    const int32_t* __restrict__ pages, int64_t n_pages, uint16_t* __restrict__ o, int64_t o_stride,
     const PrefillSeq* __restrict__ seqs, PrefillSeq single, int Hkv, float sscale, int fold) {
   constexpr int R = NW / (2 * G);     // 32-position groups per tile
   constexpr int P = QW * R;           // positions per tile
@@ -162,8 +162,12 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         rr[i] = make_uint4(v.x, v.y, v.z, v.w);
       }
     } else {
-      // block blk is page pages[blk]: rows pages[blk] * 64 .. + 63 of the int8 pool
-      const int64_t prow = int64_t(pages[blk]) * KB;
+      // block blk is page pages[kv_base + blk] (the sequence's entries of the table, kv_base
+      // the first): rows page * 64 .. + 63 of the int8 pool; an index outside the pool is
+      // clamped into it (memory stays in bounds; such a table gives meaningless output)
+      int64_t page = pages[sq.kv_base + blk];
+      page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
+      const int64_t prow = page * KB;
       const int8_t* qb = static_cast<const int8_t*>(is_k ? k_cache : v_cache) + prow * kv_stride + int64_t(g) * D;
       const float* sb = (is_k ? k_scale : v_scale) + prow * Hkv + g;
       const __amdgpu_buffer_rsrc_t rs = buf_rsrc(wave_uniform(reinterpret_cast<const uint16_t*>(qb)),
@@ -441,8 +445,9 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
 
 template <int D, int G, bool Q8>
 hipError_t launch_t(const uint16_t* q, int64_t q_stride, const void* k, const void* v, const float* ks,
-                    const float* vs, const int32_t* pages, uint16_t* o, int64_t o_stride, const PrefillSeq* seqs,
-                    PrefillSeq single, int n_seqs, int max_tiles, int Hkv, float sscale, hipStream_t s) {
+                    const float* vs, const int32_t* pages, int64_t n_pages, uint16_t* o, int64_t o_stride,
+                    const PrefillSeq* seqs, PrefillSeq single, int n_seqs, int max_tiles, int Hkv, float sscale,
+                    hipStream_t s) {
   // compute units of the device, read once (a thread-safe constant): it only decides
   // whether the grid is folded, never what a tile computes
   static const int cus = [] {
@@ -455,7 +460,7 @@ hipError_t launch_t(const uint16_t* q, int64_t q_stride, const void* k, const vo
   const int fold = int64_t(max_tiles) * Hkv * n_seqs > cus ? 1 : 0;
   const int gx = fold ? (max_tiles + 1) / 2 : max_tiles;
   hipLaunchKernelGGL((prefill_kernel<D, G, Q8>), dim3(gx, Hkv, n_seqs), dim3(NTH), 0, s, q, q_stride, k, v, ks, vs,
-                     pages, o, o_stride, seqs, single, Hkv, sscale, fold);
+                     pages, n_pages, o, o_stride, seqs, single, Hkv, sscale, fold);
   return hipGetLastError();
 }
 
@@ -473,8 +478,8 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t q_row_stride, const ui
   const float sscale = scale * 1.4426950408889634f;
 #define BI_PF(DD, GG)                                                                                    \
   if (D == DD && G == GG)                                                                              \
-    return launch_t<DD, GG, false>(q, q_row_stride, k_cache, v_cache, nullptr, nullptr, nullptr, o, o_row_stride, \
-                                   d_seqs, single, n_seqs, max_tiles, Hkv, sscale, s);
+    return launch_t<DD, GG, false>(q, q_row_stride, k_cache, v_cache, nullptr, nullptr, nullptr, 0, o,          \
+                                   o_row_stride, d_seqs, single, n_seqs, max_tiles, Hkv, sscale, s);
   BI_PF(64, 1) BI_PF(64, 2) BI_PF(64, 4)
   BI_PF(128, 1) BI_PF(128, 2) BI_PF(128, 4)
 #undef BI_PF
@@ -482,16 +487,18 @@ hipError_t launch_attn_prefill(const uint16_t* q, int64_t q_row_stride, const ui
 }
 
 hipError_t launch_attn_prefill_q8(const uint16_t* q, int64_t q_row_stride, const int8_t* k_pool, const int8_t* v_pool,
-                                  const float* k_scale, const float* v_scale, const int32_t* pages, uint16_t* o,
-                                  int64_t o_row_stride, const PrefillSeq* h_single, int max_tiles, int Hq, int Hkv,
-                                  int D, float scale, hipStream_t s) {
-  const PrefillSeq single = *h_single;
+                                  const float* k_scale, const float* v_scale, const int32_t* pages, int64_t n_pages,
+                                  uint16_t* o, int64_t o_row_stride, const PrefillSeq* d_seqs,
+                                  const PrefillSeq* h_single, int n_seqs, int max_tiles, int Hq, int Hkv, int D,
+                                  float scale, hipStream_t s) {
+  PrefillSeq single{};
+  if (h_single) single = *h_single;
   const int G = Hq / Hkv;
   const float sscale = scale * 1.4426950408889634f;
 #define BI_PF(DD, GG)                                                                                    \
   if (D == DD && G == GG)                                                                              \
-    return launch_t<DD, GG, true>(q, q_row_stride, k_pool, v_pool, k_scale, v_scale, pages, o, o_row_stride, \
-                                  nullptr, single, 1, max_tiles, Hkv, sscale, s);
+    return launch_t<DD, GG, true>(q, q_row_stride, k_pool, v_pool, k_scale, v_scale, pages, n_pages, o,        \
+                                  o_row_stride, d_seqs, single, n_seqs, max_tiles, Hkv, sscale, s);
   BI_PF(64, 1) BI_PF(64, 2) BI_PF(64, 4)
   BI_PF(128, 1) BI_PF(128, 2) BI_PF(128, 4)
 #undef BI_PF

@@ -105,15 +105,27 @@ hipError_t launch_attn_decode_po(const uint16_t* q, int64_t q_row_stride, const 
 // [rows, Hkv]; pages of 64 rows; page tables are int32.
 hipError_t launch_kv_quant(const uint16_t* k, const uint16_t* v, const int64_t* dst_row, int64_t rows, int Hkv,
                            int D, int8_t* kq, int8_t* vq, float* ks, float* vs, hipStream_t s);
+// Paged int8 attention.  pages: page indices; a sequence's entries start at its
+// PrefillSeq / DecodeSeq kv_base / kv_offset (d_seqs given), else at 0 (prefill, one
+// sequence by value) or b * max_pages (decode, per-request tables).  Page indices outside
+// 0 .. n_pages - 1 are clamped into the pool.
 hipError_t launch_attn_prefill_q8(const uint16_t* q, int64_t q_row_stride, const int8_t* k_pool, const int8_t* v_pool,
-                                  const float* k_scale, const float* v_scale, const int32_t* pages, uint16_t* o,
-                                  int64_t o_row_stride, const PrefillSeq* h_single, int max_tiles, int Hq, int Hkv,
-                                  int D, float scale, hipStream_t s);
-hipError_t launch_attn_decode_po_q8(const uint16_t* q, const int8_t* k_pool, const int8_t* v_pool,
-                                    const float* k_scale, const float* v_scale, const int32_t* block_tables,
-                                    int max_pages, const int32_t* kv_len, const int32_t* d_order, int B,
+                                  const float* k_scale, const float* v_scale, const int32_t* pages, int64_t n_pages,
+                                  uint16_t* o, int64_t o_row_stride, const PrefillSeq* d_seqs,
+                                  const PrefillSeq* h_single, int n_seqs, int max_tiles, int Hq, int Hkv, int D,
+                                  float scale, hipStream_t s);
+hipError_t launch_attn_decode_po_q8(const uint16_t* q, int64_t q_row_stride, const int8_t* k_pool,
+                                    const int8_t* v_pool, const float* k_scale, const float* v_scale,
+                                    const int32_t* block_tables, int max_pages, int64_t n_pages,
+                                    const DecodeSeq* d_seqs, const int32_t* kv_len, const int32_t* d_order, int B,
                                     int64_t max_kv_len, int Hq, int Hkv, int D, float scale, uint16_t* o,
-                                    hipStream_t s);
+                                    int64_t o_row_stride, hipStream_t s);
+// Paged int8 append: token r (bf16 k, v rows r of [rows, Hkv, D]) at position pos[r] of a
+// sequence whose table entries start at entry_plus_pos[r] - pos[r].  A page index outside
+// the pool writes nothing.
+hipError_t launch_kv_quant_paged(const uint16_t* k, const uint16_t* v, const int64_t* entry_plus_pos,
+                                 const int32_t* pos, const int32_t* pages, int64_t n_pages, int64_t rows, int Hkv,
+                                 int D, int8_t* kq, int8_t* vq, float* ks, float* vs, hipStream_t s);
 
 // Sampler settings (mirrors bi_sampling of the public header).
 struct BiSampling {

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void rope_kv_kernel(const uint16_t* __restrict
     s_sin[threadIdx.x] = s;
   }
   __syncthreads();
-  const int64_t kvr = kv_row[r];
+  const int64_t kvr = kv_row ? kv_row[r] : r;  // no row list: k and v go to rows r of the pools
   const uint16_t* src = qkv + r * int64_t(Hq + 2 * Hkv) * D;
   const int n_rot = (Hq + Hkv) * PCH;
   const int n_items = n_rot + Hkv * VCH;

@@ -9,7 +9,7 @@
 // build.  Everything here is per row: a row's token depends only on its
 // logits, its history, its seed and its position, never on the batch.
 //
-// Sampler (one 256-thread work-group per row):
+// Sampler (one 512-thread work-group per row):
 //  1. penalties in fp32 for each distinct history token (repeat: l > 0 ->
 //     l / r else l * r; then l - (presence + count * frequency)), written with
 //     contraction off so no fused multiply-add changes a rounding;

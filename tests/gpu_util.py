@@ -36,3 +36,28 @@ def assert_bitwise(a, b, what=""):
         first = tuple(diff[0]) if diff is not None and len(diff) else None
         n = len(diff) if diff is not None else "shape"
         raise AssertionError(f"{what}: not bitwise equal ({n} differing, first at {first})")
+
+
+def nan_filled(shape, dtype, device="cuda"):
+    """A device tensor whose every byte is 0xFF (NaN for bf16 and fp32): an output or
+    workspace a kernel forgets to write, or reads before writing, shows up as NaN."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    t.view(torch.uint8).fill_(0xFF)
+    return t
+
+
+def forward_poisoned(blk, x, seqs, k_pool, v_pool):
+    """Block.forward with a NaN-filled workspace and output (the stage views stay valid)."""
+    lay = bi.block_workspace(blk.cfg, seqs)
+    ws = nan_filled((max(int(lay.total), 256),), torch.uint8, x.device)
+    y = nan_filled(tuple(x.shape), torch.bfloat16, x.device)
+    return blk.forward(x, seqs, k_pool, v_pool, y=y, ws=ws)
+
+
+def split_rows(y_bits, seqs):
+    """Per-sequence row blocks of a block output."""
+    out, row = [], 0
+    for s in seqs:
+        out.append(y_bits[row:row + int(s["q_len"])])
+        row += int(s["q_len"])
+    return out

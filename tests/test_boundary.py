@@ -239,3 +239,76 @@ def test_block_forward_checks():
     assert call(cfg_=bad) == UNSUP
     w4 = bi.BlockConfig(2560, 32, 8, 128, 9728, int4=True).c()
     assert call(cfg_=w4) == NULL                        # int4 weights need scales
+
+
+def test_grid_limits_rejected_before_launch():
+    """Sizes whose launch grid would not fit (more than 2^32 work-items along a dimension, or
+    more than 65535 along y / z) return BI_ERR_UNSUPPORTED from the checks."""
+    L = bi.lib()
+    assert L.bi_rmsnorm(P16, P16b, P16c, (1 << 26) - 1023, 256, 1e-6, NUL) == UNSUP
+    assert L.bi_rope_kv(P16, P16b, P16c, P16, P16b, P16c, 1 << 24, 32, 8, 128, 1e6, NUL) == UNSUP
+    assert L.bi_kv_append_q8(P16, P16b, P16c, 1 << 26, 8, 128, P16, P16b, P16c, P16, NUL) == UNSUP
+    # 2^23 query tiles of 32 positions (group 4) at the end of a long context
+    assert L.bi_attn_prefill(P16, P16, P16b, P16c, 0, (1 << 28), 32, 8, 128, 0.088, NUL) == UNSUP
+    assert L.bi_gemm(P16, P16b, P16c, 1 << 30, 1 << 13, 64, NUL) == UNSUP  # 2^27 tiles
+
+
+def _block_call(seqs, cfg=None, rows=1 << 40):
+    L = bi.lib()
+    cfg = cfg or bi.BlockConfig(2560, 32, 8, 128, 9728, 1e-6, 1e6)
+    w = bi.bi_block_weights()
+    w.gamma1 = P16; w.gamma2 = P16
+    for f in ("qkv", "o", "gate_up", "down"):
+        setattr(w, f, bi.bi_weight(0x500000, None))
+    arr = bi._seq_array(seqs)
+    lay = bi.block_workspace(cfg, seqs)
+    pool = bi.bi_kv_pool(0x600000, 0x700000, rows)
+    return L.bi_block_forward(ctypes.byref(cfg.c()), ctypes.byref(w), arr, len(seqs), P16, ctypes.byref(pool), P16b,
+                              P16c, P16, lay.total, NUL)
+
+
+def test_block_forward_grid_limits():
+    """bi_block_forward checks every launch's grid before the first kernel is enqueued:
+    too many decode requests for the combine grid, too many tokens for the RoPE grid, a decode
+    longer than 2^30 keys."""
+    many = [dict(q_len=1, ctx_len=10, kv_base=20 * i) for i in range(65536)]
+    assert _block_call(many) == UNSUP
+    assert _block_call([dict(q_len=1 << 24, ctx_len=0, kv_base=0)], bi.BlockConfig(256, 4, 4, 64)) == UNSUP
+    assert _block_call([dict(q_len=1, ctx_len=(1 << 30), kv_base=0)]) == UNSUP
+
+
+class _Fake:
+    """Stand-in for a tensor in the CPU tests of Block.check_args (shape checks come first)."""
+
+
+def test_block_binding_checks_shapes_before_launch():
+    """Block.forward checks x, y and the pools against the configuration before it calls the
+    library (a mismatch would make the kernels read or write out of bounds)."""
+    torch = pytest.importorskip("torch")
+    cfg = bi.BlockConfig(256, 4, 2, 64, 0)
+    blk = bi.Block(cfg, {"gamma1": torch.zeros(256, dtype=torch.bfloat16),
+                         "w_qkv": torch.zeros((512, 256), dtype=torch.bfloat16),
+                         "w_o": torch.zeros((256, 256), dtype=torch.bfloat16)})
+    seqs = [dict(q_len=3, ctx_len=0, kv_base=0), dict(q_len=1, ctx_len=5, kv_base=16)]
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    kp = torch.zeros((32, 2, 64), dtype=torch.bfloat16)
+    bad = [
+        dict(x=torch.zeros((5, 256), dtype=torch.bfloat16)),            # rows != sum of q_len
+        dict(x=torch.zeros((4, 128), dtype=torch.bfloat16)),            # width != hidden
+        dict(y=torch.zeros((3, 256), dtype=torch.bfloat16)),            # y shape
+        dict(k_pool=torch.zeros((32, 4, 32), dtype=torch.bfloat16)),    # other head layout
+        dict(v_pool=torch.zeros((31, 2, 64), dtype=torch.bfloat16)),    # pools differ
+        dict(k_pool=torch.zeros((20, 2, 64), dtype=torch.bfloat16),
+             v_pool=torch.zeros((20, 2, 64), dtype=torch.bfloat16)),    # second sequence needs row 21
+    ]
+    for b in bad:
+        args = dict(x=x, k_pool=kp, v_pool=kp.clone(), y=None)
+        args.update(b)
+        with pytest.raises(ValueError) as ei:
+            blk.check_args(args["x"], seqs, args["k_pool"], args["v_pool"], args["y"])
+        assert "device" not in str(ei.value), ei.value
+    # right shapes on the host: rejected as not device tensors, still before any launch
+    with pytest.raises(ValueError, match="device"):
+        blk.forward(x, seqs, kp, kp.clone())
+    with pytest.raises(TypeError):
+        blk.check_args(x, seqs, kp, kp.clone(), y=_Fake())

@@ -21,6 +21,7 @@ import oracle
 from oracle import sampling as S
 from invariant_deterministic_amd import bi, synth
 from tests.gpu_util import announce, assert_bitwise, bits, dev, device
+from tests.util import assert_within_tolerance
 
 pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -158,6 +159,14 @@ def test_step_after_block():
     n = bi.rmsnorm(dev(x), dev(gamma), 1e-6)
     logits = bi.gemm(n, w)
     lg = bits(logits)
+    # final norm and LM-head logits against the oracle, per element, on sampled rows (the
+    # whole vocabulary, in slices of the weight)
+    nb = bits(n)
+    assert_within_tolerance(nb, oracle.rmsnorm(x, gamma, 1e-6), "final RMSNorm")
+    rows = np.array([0, 17, 42, M - 1])
+    for c0 in range(0, V, 16384):
+        wc = bits(w[c0:c0 + 16384])
+        assert_within_tolerance(lg[rows, c0:c0 + len(wc)], oracle.gemm(nb[rows], wc), f"LM head logits {c0}..")
     seeds = np.arange(M, dtype=np.uint64) + 99
     pos = np.arange(M) + 4000
     prm = dict(temperature=0.8, top_k=50, top_p=0.95, min_p=0.05, repeat=1.0, presence=0.0, frequency=0.0)
