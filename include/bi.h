@@ -207,6 +207,23 @@ bi_status bi_attn_decode(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* 
                          int B, int64_t max_kv_len, int Hq, int Hkv, int D, float scale,
                          void* ws, size_t ws_bytes, bi_bf16* o, hipStream_t stream);
 
+/* bi_attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same kernels and the same bits, with the workspace taken from a fixed
+ * scratch array the library holds on each GPU (32 MiB, kept until the process
+ * ends; its device address is looked up once per device, on the first call
+ * with that device current).  Calls nothing that allocates.  Sizes whose
+ * workspace (bi_attn_decode_workspace) exceeds 32 MiB return
+ * BI_ERR_WORKSPACE -- e.g. 256 requests of up to 8192 keys (21 MB) and 64 of
+ * up to 32768 keys (17 MB) fit.  All calls on one GPU share its scratch, so
+ * calls that overlap in time on one GPU (other streams or threads) race and
+ * must be ordered by the caller.  Other arguments and errors as
+ * bi_attn_decode.                                                            */
+bi_status bi_attn_decode_noalloc(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* v_all,
+                                 const int64_t* kv_offset, const int32_t* kv_len,
+                                 int B, int64_t max_kv_len, int Hq, int Hkv, int D, float scale,
+                                 bi_bf16* o, hipStream_t stream);
+
 /* ------------------------------------- decode attention in prefill key order
  * The same result as bi_attn_decode, computed with exactly the operations
  * bi_attn_prefill performs for a query at position L_b - 1 (its 64-key blocks

@@ -90,6 +90,8 @@ _SIGNATURES = {
     "bi_attn_decode_workspace": (c_size_t, [c_int, c_int64, c_int, c_int]),
     "bi_attn_decode": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int,
                                c_int, c_int, c_float, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "bi_attn_decode_noalloc": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int,
+                                       c_int, c_int, c_float, c_void_p, c_void_p]),
     "bi_attn_decode_prefill_order": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
                                              c_int64, c_int, c_int, c_int, c_float, c_void_p, c_void_p]),
     "bi_kv_append_q8": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int, c_int, c_void_p, c_void_p, c_void_p,
@@ -329,6 +331,21 @@ def attn_decode(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq, Hkv, D, scal
     _check(lib().bi_attn_decode(_ptr(q), _ptr(k_all), _ptr(v_all), _ptr(kv_offset), _ptr(kv_len), B,
                                 int(max_kv_len), Hq, Hkv, D, float(scale), _ptr(ws), ws.numel(), _ptr(out),
                                 _stream()), "bi_attn_decode")
+    return out
+
+
+def attn_decode_noalloc(q, k_all, v_all, kv_offset, kv_len, max_kv_len, Hq, Hkv, D, scale, out):
+    """bi_attn_decode with the library's fixed per-device scratch as workspace; `out` must be
+    given (the call allocates nothing, and neither does this wrapper)."""
+    _dev(q, BF16, "q"); _dev(k_all, BF16, "k_all"); _dev(v_all, BF16, "v_all")
+    _dev(kv_offset, torch.int64, "kv_offset"); _dev(kv_len, torch.int32, "kv_len")
+    B = q.shape[0]
+    if kv_offset.shape != (B,) or kv_len.shape != (B,):
+        raise ValueError("kv_offset / kv_len must have one entry per query row")
+    out = _out(out, q.shape, BF16, q)
+    _check(lib().bi_attn_decode_noalloc(_ptr(q), _ptr(k_all), _ptr(v_all), _ptr(kv_offset), _ptr(kv_len), B,
+                                        int(max_kv_len), Hq, Hkv, D, float(scale), _ptr(out), _stream()),
+           "bi_attn_decode_noalloc")
     return out
 
 

@@ -419,6 +419,26 @@ bi_status bi_attn_decode(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* 
                                                 Hq, Hkv, D, scale, ws, o, stream));
 }
 
+bi_status bi_attn_decode_noalloc(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* v_all,
+                                 const int64_t* kv_offset, const int32_t* kv_len, int B, int64_t max_kv_len, int Hq,
+                                 int Hkv, int D, float scale, bi_bf16* o, hipStream_t stream) {
+  if (!q || !k_all || !v_all || !kv_offset || !kv_len || !o) return BI_ERR_NULL;
+  if (B < 1 || max_kv_len < 1) return BI_ERR_SHAPE;
+  if (B > kMaxGridYZ || max_kv_len > kMaxDecodeLen || Hkv > kMaxGridYZ) return BI_ERR_UNSUPPORTED;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv) return BI_ERR_SHAPE;
+  if (!head_shape_ok(Hq, Hkv, D, 8)) return BI_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return BI_ERR_SHAPE;
+  const int64_t run_keys = int64_t(bi::kKvSplit) * bi::kDecodeRun;
+  if (int64_t(B) * ((max_kv_len + run_keys - 1) / run_keys) > kMaxDecodeRuns) return BI_ERR_UNSUPPORTED;
+  // the partials must fit the library's fixed scratch
+  if (bi::decode_workspace_bytes(B, max_kv_len, Hq, D) > bi::kDecodeScratchBytes) return BI_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_all) || !aligned16(v_all) || !aligned16(o) || !aligned8(kv_offset) ||
+      (reinterpret_cast<uintptr_t>(kv_len) & 3u))
+    return BI_ERR_ALIGN;
+  return from_hip(bi::launch_attn_decode_noalloc(q, k_all, v_all, kv_offset, kv_len, B, max_kv_len, Hq, Hkv, D,
+                                                 scale, o, stream));
+}
+
 bi_status bi_attn_decode_prefill_order(const bi_bf16* q, const bi_bf16* k_all, const bi_bf16* v_all,
                                        const int64_t* kv_offset, const int32_t* kv_len,
                                        const int32_t* order, int B, int64_t max_kv_len, int Hq,

@@ -45,6 +45,8 @@
 // M = max m_s; w_s = exp2(m_s - M); O = sum w_s o_s and Lsum = sum w_s l_s
 // as fmas in ascending s.  The combine kernel, one thread per (request, head,
 // dim), merges the runs and writes bf16(O / Lsum).
+#include <mutex>
+
 #include "bi_dev.h"
 #include "bi_internal.h"
 
@@ -525,6 +527,48 @@ hipError_t launch_attn_decode(const uint16_t* q, int64_t q_row_stride, const uin
   const WsParts w = ws_parts(ws, B, max_kv_len, Hq, D, nullptr);
   return run_decode(q, q_row_stride, k_all, v_all, d_seqs, d_runs, nullptr, n_runs, B, max_kv_len, Hq, Hkv, D,
                     scale, w, o, o_row_stride, s);
+}
+
+// Scratch of the allocation-free decode entry point: a file-scope device array, one copy
+// per GPU, held until the process ends.  In host code its name stands for no device
+// address: kernels get the address hipGetSymbolAddress returns for the current device,
+// looked up once per device and kept in scratch_dev.  Every call on a GPU shares that
+// GPU's copy (calls that overlap on one GPU race on it).  Nothing in it has to start at
+// zero: the list kernel writes the run count and list, the unit kernel every partial the
+// combine kernel reads, all within the call.
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+static hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_attn_decode_noalloc(const uint16_t* q, const uint16_t* k_all, const uint16_t* v_all,
+                                      const int64_t* kv_offset, const int32_t* kv_len, int B, int64_t max_kv_len,
+                                      int Hq, int Hkv, int D, float scale, uint16_t* o, hipStream_t s) {
+  if (decode_workspace_bytes(B, max_kv_len, Hq, D) > kDecodeScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return e;
+  return launch_attn_decode_arrays(q, k_all, v_all, kv_offset, kv_len, B, max_kv_len, Hq, Hkv, D, scale, ws, o, s);
 }
 
 hipError_t launch_attn_decode_arrays(const uint16_t* q, const uint16_t* k_all,

@@ -90,6 +90,12 @@ hipError_t launch_attn_decode_arrays(const uint16_t* q, const uint16_t* k_all,
                                      const int32_t* kv_len, int B, int64_t max_kv_len, int Hq,
                                      int Hkv, int D, float scale, void* ws, uint16_t* o,
                                      hipStream_t s);
+// The same with the library's own per-device scratch (kDecodeScratchBytes) as workspace:
+// allocates nothing.  Fails with hipErrorInvalidValue when the workspace would not fit.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t launch_attn_decode_noalloc(const uint16_t* q, const uint16_t* k_all, const uint16_t* v_all,
+                                      const int64_t* kv_offset, const int32_t* kv_len, int B, int64_t max_kv_len,
+                                      int Hq, int Hkv, int D, float scale, uint16_t* o, hipStream_t s);
 
 // Decode attention in the prefill kernel's key order (bitwise equal to prefill
 // for the same query).  Request descriptors come from d_seqs, or, when d_seqs

@@ -62,6 +62,10 @@ hipError_t launch_attn_decode_arrays(const uint16_t*, const uint16_t*, const uin
                                      hipStream_t) {
   return logged("decode_split");
 }
+hipError_t launch_attn_decode_noalloc(const uint16_t*, const uint16_t*, const uint16_t*, const int64_t*,
+                                      const int32_t*, int, int64_t, int, int, int, float, uint16_t*, hipStream_t) {
+  return logged("decode_noalloc");
+}
 hipError_t launch_attn_decode_po(const uint16_t*, int64_t, const uint16_t*, const uint16_t*, const DecodeSeq*,
                                  const int64_t*, const int32_t*, const int32_t*, int, int64_t, int, int, int, float,
                                  uint16_t*, int64_t, hipStream_t) {

@@ -312,3 +312,16 @@ def test_block_binding_checks_shapes_before_launch():
         blk.forward(x, seqs, kp, kp.clone())
     with pytest.raises(TypeError):
         blk.check_args(x, seqs, kp, kp.clone(), y=_Fake())
+
+
+def test_noalloc_decode_checks():
+    """bi_attn_decode_noalloc refuses, before any launch, a step whose partials would not fit
+    the library's 32 MiB scratch, and otherwise checks as bi_attn_decode."""
+    L = bi.lib()
+    args = lambda B=4, maxl=1000, D=128, q=P16: (q, P16b, P16c, P16, P16b, B, maxl, 32, 8, D, 0.088, P16c, NUL)
+    assert bi.attn_decode_workspace(1024, 32768, 32, 128) > (32 << 20)
+    assert L.bi_attn_decode_noalloc(*args(B=1024, maxl=32768)) == WS
+    assert L.bi_attn_decode_noalloc(*args(B=0)) == SHAPE
+    assert L.bi_attn_decode_noalloc(*args(D=80)) == UNSUP
+    assert L.bi_attn_decode_noalloc(*args(q=NUL)) == NULL
+    assert L.bi_attn_decode_noalloc(*args(q=MIS)) == ALIGN
