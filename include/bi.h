@@ -78,10 +78,11 @@ int bi_kv_split_size(void);
 void bi_gemm_tile(int out[3]);
 
 /* Column-tile width the GEMMs use for a weight of N rows: 256, or 192 for
- * bf16 weights (weight_format BI_WEIGHTS_BF16) of at most 3072 rows, where
- * 256-wide tiles would leave most compute units idle.  A function of the
- * weight alone, never of M; the SwiGLU forms always pair 128 gate and 128 up
- * rows per tile.  Returns 0 for N < 1.  (No element's bits depend on it.)   */
+ * bf16 weights (weight_format BI_WEIGHTS_BF16) of at most 3072 rows and int4
+ * weights of at most 4096 rows, where 256-wide tiles would leave many compute
+ * units idle.  A function of the weight alone, never of M; the SwiGLU forms
+ * always pair 128 gate and 128 up rows per tile.  Returns 0 for N < 1.  (No
+ * element's bits depend on it.)                                             */
 int bi_gemm_tile_cols(int64_t N, int weight_format);
 
 /* ------------------------------------------------------------------ RMSNorm

@@ -274,7 +274,7 @@ void bi_gemm_tile(int out[3]) {
 
 int bi_gemm_tile_cols(int64_t N, int weight_format) {
   if (N < 1) return 0;
-  return weight_format == BI_WEIGHTS_BF16 ? bi::gemm_tile_n(N, bi::kEpiPlain) : bi::kGemmBN;
+  return weight_format == BI_WEIGHTS_BF16 ? bi::gemm_tile_n(N, bi::kEpiPlain) : bi::gemm_w4_tile_n(N, bi::kEpiPlain);
 }
 
 bi_status bi_rmsnorm(const bi_bf16* x, const bi_bf16* gamma, bi_bf16* y, int64_t rows,

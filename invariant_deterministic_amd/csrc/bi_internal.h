@@ -20,6 +20,9 @@ constexpr int64_t kGemmNarrowN = 3072;
 constexpr int64_t kGemmMaxK = int64_t(1) << 22;
 // column-tile width of the bf16 GEMM for a weight of N rows (epi: kEpi*)
 int gemm_tile_n(int64_t N, int epi);
+// int4 weights of at most kGemmW4NarrowN rows use kGemmBNNarrow-wide column tiles
+constexpr int64_t kGemmW4NarrowN = 4096;
+int gemm_w4_tile_n(int64_t N, int epi);
 
 // Decode attention: fixed key/value split size.
 constexpr int kKvSplit = 256;

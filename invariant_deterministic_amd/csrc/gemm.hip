@@ -5,8 +5,8 @@
 // ("Deterministic and bit-exact inference", field `technical`) makes
 // batch-invariant.  The invariance argument here:
 //  * one tile shape and one instruction stream for every M: 256 x 256 x 64, or
-//    256 x 192 x 64 for bf16 weights of at most 3072 rows (the width is a
-//    function of the weight's row count alone); there is no M-dependent
+//    256 x 192 x 64 for bf16 weights of at most 3072 rows and int4 weights of at
+//    most 4096 rows (the width is a function of the weight alone); there is no M-dependent
 //    dispatch, no split-K and no stream-K, and rows past M are handled by
 //    clamping their loads and masking their stores in the same instruction
 //    stream;
@@ -23,7 +23,9 @@
 // de-quantisation kernels with atomic additions): each thread expands one
 // 32-element group -- code * fp16 scale, exact in fp32, one rounding to bf16
 // -- straight into the same LDS tile the bf16 path uses, so the int4 GEMM is
-// bit-identical to the bf16 GEMM on the de-quantised weight.
+// bit-identical to the bf16 GEMM on the de-quantised weight.  The expansion
+// takes ~2.4 VALU instructions per element (two codes per bit operation as fp16
+// pairs, one mixed-precision fma each, one packed bf16 conversion per pair).
 //
 // Int4 weights, register-staged schedule.  Data flow: global -> registers
 // (prefetch of step k+1 during step k) -> LDS
@@ -89,23 +91,46 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * BK + ((chunk ^ ((row >> 1) & 7)) << 3);
 }
 
-// Expand one int4 group (16 bytes = 32 codes, one fp16 scale) into four
-// bf16 16-byte chunks of tile row `row`: w = bf16(code * scale).
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two fp32 values -> packed bf16 pair (one v_cvt_pk_bf16_f32), round to nearest even.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// De-quantise 8 int4 codes (one little-endian word; nibble e is element e) with the
+// group's scale s: w_e = bf16(code_e * s), code_e the two's-complement nibble.  Each
+// code becomes the fp16 value 1024 + 8 + code (the exponent field of 1024, the nibble with
+// its top bit flipped in the low mantissa bits: two codes per word op, no conversion
+// instruction), then fma(1024 + 8 + code, s, -1032 s) = code * s exactly in fp32 (the
+// product has at most 15 significant bits, -1032 s at most 19; one rounding of an exact
+// value), rounded once to bf16: the bits of bf16(float(code) * s).
+// sc = s as fp32, nb = -1032 * sc (exact).
+__device__ __forceinline__ uint4 dequant8(uint32_t word, float sc, float nb) {
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // the fp16 pair (1024 + 8 + code_j, 1024 + 8 + code_{j+4})
+    const f16x2 p = __builtin_bit_cast(f16x2, ((word >> (4 * j)) & 0x000F000Fu) ^ 0x64086408u);
+    f[j] = __builtin_fmaf(float(p[0]), sc, nb);
+    f[j + 4] = __builtin_fmaf(float(p[1]), sc, nb);
+  }
+  return make_uint4(pk_bf16(f[0], f[1]), pk_bf16(f[2], f[3]), pk_bf16(f[4], f[5]), pk_bf16(f[6], f[7]));
+}
+
+// Expand one int4 group (16 bytes = 32 codes, one fp16 scale) into four bf16 16-byte
+// chunks of tile row `row`.
 __device__ __forceinline__ void dequant_group_to_lds(const uint4& rq, uint16_t rs, uint16_t* sW,
                                                      int row, int half) {
   const float s = float(__builtin_bit_cast(_Float16, rs));
+  const float nb = -1032.0f * s;
   const uint32_t words[4] = {rq.x, rq.y, rq.z, rq.w};
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float f[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // nibble e of the little-endian word is element 8c + e of the group
-      const int code = int(words[c] << (28 - 4 * e)) >> 28;
-      f[e] = float(code) * s;  // exact: |code| <= 8, s has 11 significant bits
-    }
-    *reinterpret_cast<uint4*>(sW + lds_off(row, half * 4 + c)) = pack8(f);
-  }
+  for (int c = 0; c < 4; ++c)
+    *reinterpret_cast<uint4*>(sW + lds_off(row, half * 4 + c)) = dequant8(words[c], s, nb);
 }
 
 // Epilogues.  kEpiPlain: C = bf16(acc).  kEpiResid: C = bf16(R + bf16(acc)), the residual
@@ -176,14 +201,16 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[BNT / 64][2], uin
   }
 }
 
-// int4-weight GEMM, register-staged schedule (see the file comment).
-template <int EPI>
+// int4-weight GEMM, register-staged schedule (see the file comment), BM x BNT x BK tiles.
+template <int EPI, int BNT>
 __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restrict__ A,
                                                         const uint8_t* __restrict__ Wq,
                                                         const uint16_t* __restrict__ Ws,
                                                         const uint16_t* R,  // may alias C (resid)
                                                         uint16_t* C, int M, int N, int K,
                                                         int tiles_n, int n_tiles) {
+  static_assert(BNT == 256 || (BNT == 192 && EPI != kEpiGated), "tile width");
+  constexpr int NB = BNT / 64;  // 32-column blocks per wave (two waves along N)
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];
 
   const int tile = tile_of(blockIdx.x, n_tiles, tiles_n);
@@ -193,12 +220,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int wn = wave & 1;   // 128 output columns
+  const int wn = wave & 1;   // BNT / 2 output columns
   const int wm = wave >> 1;  // 64 output rows
 
   // ---- global load assignment
   // A tile: 256 rows x 8 chunks; thread t loads chunk (t & 7) of rows (t >> 3) + 64 i.
-  // W tile: thread t expands the 32-code group t & 1 of tile row t >> 1.
+  // W tile: thread t expands the 32-code group t & 1 of tile row t >> 1.  A 192-wide tile
+  // uses rows 0 .. 191 of the LDS tile; the threads of rows 192 .. 255 expand a clamped row
+  // into the unused rest (no branch in the loop).
   // Rows past M (past N for W) are clamped: computed, never stored.
   const int ld_chunk = t & 7;
   const int ld_row = t >> 3;
@@ -208,7 +237,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
   int a_r2 = min(tm * BM + ld_row + 128, a_last), a_r3 = min(tm * BM + ld_row + 192, a_last);
   const int q_row = t >> 1;
   const int q_half = t & 1;
-  const int q_r = min(w_row<EPI>(tn, q_row, N), w_last);
+  const int q_r = min(w_row<EPI, BNT>(tn, q_row, N), w_last);
   const uint8_t* q_src = Wq + int64_t(q_r) * (K / 2) + q_half * 16;
   const uint16_t* s_src = Ws + int64_t(q_r) * (K / 32) + q_half;
 
@@ -237,9 +266,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
     dequant_group_to_lds(rq, rs, sW, q_row, q_half);                                        \
   } while (0)
 
-  f32x16 acc[4][2];
+  f32x16 acc[NB][2];
 #pragma unroll
-  for (int bn = 0; bn < 4; ++bn)
+  for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
     for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
@@ -261,13 +290,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
     if constexpr (NBM == 0) {
       if constexpr (SAT >= 0) store();
     } else {
-      bf16x8 wf[2][4], af[2][NBM];
+      bf16x8 wf[2][NB], af[2][NBM];
 #pragma unroll
       for (int bm = 0; bm < NBM; ++bm)
         af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 64 + bm * 32 + frag_row, frag_chunk));
 #pragma unroll
-      for (int bn = 0; bn < 4; ++bn)
-        wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + lds_off(wn * 128 + bn * 32 + frag_row, frag_chunk));
+      for (int bn = 0; bn < NB; ++bn)
+        wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + lds_off(wn * (BNT / 2) + bn * 32 + frag_row, frag_chunk));
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
@@ -279,12 +308,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
             af[nb][bm] = *reinterpret_cast<const bf16x8*>(
                 sA + lds_off(wm * 64 + bm * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
 #pragma unroll
-          for (int bn = 0; bn < 4; ++bn)
+          for (int bn = 0; bn < NB; ++bn)
             wf[nb][bn] = *reinterpret_cast<const bf16x8*>(
-                sW + lds_off(wn * 128 + bn * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
+                sW + lds_off(wn * (BNT / 2) + bn * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
         }
 #pragma unroll
-        for (int bn = 0; bn < 4; ++bn)
+        for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
           for (int bm = 0; bm < NBM; ++bm)
             acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][bn], af[cb][bm], acc[bn][bm], 0, 0, 0);
@@ -292,11 +321,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
         if (kk + 1 < BK / 16) {
           // one fragment read between consecutive MFMAs
 #pragma unroll
-          for (int i = 0; i < NBM + 4; ++i) {
+          for (int i = 0; i < NBM + NB; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-          if constexpr (4 * NBM > NBM + 4) __builtin_amdgcn_sched_group_barrier(0x008, 4 * NBM - NBM - 4, 0);
+          if constexpr (NB * NBM > NBM + NB) __builtin_amdgcn_sched_group_barrier(0x008, NB * NBM - NBM - NB, 0);
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -323,7 +352,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
   else if (nbm == 1) run(std::integral_constant<int, 1>{});
   else run(std::integral_constant<int, 0>{});
 
-  store_tile<EPI, BN>(acc, C, R, M, N, tm, tn, wm, wn, lane);
+  store_tile<EPI, BNT>(acc, C, R, M, N, tm, tn, wm, wn, lane);
 #undef BI_LOAD_GLOBAL
 #undef BI_STORE_LDS
 }
@@ -491,6 +520,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
 // Column-tile width of the bf16 GEMM for a weight of N rows: 256, or 192 for weights of at
 // most kGemmNarrowN rows (not the gated form).  It depends on the weight alone, never on M.
 int gemm_tile_n(int64_t N, int epi) { return (epi != kEpiGated && N <= kGemmNarrowN) ? kGemmBNNarrow : BN; }
+// The same for int4 weights: 192-wide tiles up to kGemmW4NarrowN rows.
+int gemm_w4_tile_n(int64_t N, int epi) { return (epi != kEpiGated && N <= kGemmW4NarrowN) ? kGemmBNNarrow : BN; }
 
 // epi: kEpiPlain / kEpiResid (R [M, N]) / kEpiGated (N = F outputs, W [2F, K], F % 128 == 0)
 hipError_t launch_gemm_ex(const uint16_t* A, const uint16_t* W, const uint16_t* R, uint16_t* C, int64_t M,
@@ -513,16 +544,18 @@ hipError_t launch_gemm_ex(const uint16_t* A, const uint16_t* W, const uint16_t* 
 
 hipError_t launch_gemm_w4_ex(const uint8_t* Wq, const uint16_t* Ws, const uint16_t* A, const uint16_t* R,
                              uint16_t* C, int64_t M, int64_t N, int64_t K, int epi, hipStream_t s) {
+  const int bnt = gemm_w4_tile_n(N, epi);
   const int tiles_m = int((M + BM - 1) / BM);
-  const int tiles_n = epi == kEpiGated ? int(N / 128) : int((N + BN - 1) / BN);
+  const int tiles_n = epi == kEpiGated ? int(N / 128) : int((N + bnt - 1) / bnt);
   const int n_tiles = tiles_m * tiles_n;
-#define BI_GEMM(E)                                                                                               \
-  if (epi == E) {                                                                                                \
-    hipLaunchKernelGGL(gemm_w4_kernel<E>, dim3(n_tiles), dim3(NT), 0, s, A, Wq, Ws, R, C, int(M), int(N), int(K), \
-                       tiles_n, n_tiles);                                                                        \
-    return hipGetLastError();                                                                                    \
+#define BI_GEMM(E, T)                                                                                          \
+  if (epi == E && bnt == T) {                                                                                  \
+    hipLaunchKernelGGL((gemm_w4_kernel<E, T>), dim3(n_tiles), dim3(NT), 0, s, A, Wq, Ws, R, C, int(M), int(N),   \
+                       int(K), tiles_n, n_tiles);                                                              \
+    return hipGetLastError();                                                                                  \
   }
-  BI_GEMM(kEpiPlain) BI_GEMM(kEpiResid) BI_GEMM(kEpiGated)
+  BI_GEMM(kEpiPlain, BN) BI_GEMM(kEpiResid, BN) BI_GEMM(kEpiGated, BN)
+  BI_GEMM(kEpiPlain, kGemmBNNarrow) BI_GEMM(kEpiResid, kGemmBNNarrow)
 #undef BI_GEMM
   return hipErrorInvalidValue;
 }

@@ -18,6 +18,7 @@ static hipError_t logged(const char* name) {
 }
 
 int gemm_tile_n(int64_t N, int epi) { return (epi != kEpiGated && N <= kGemmNarrowN) ? kGemmBNNarrow : kGemmBN; }
+int gemm_w4_tile_n(int64_t N, int epi) { return (epi != kEpiGated && N <= kGemmW4NarrowN) ? kGemmBNNarrow : kGemmBN; }
 int prefill_positions_per_tile(int group) { return 128 / group; }
 size_t decode_workspace_bytes(int B, int64_t max_kv_len, int Hq, int D) {
   const int64_t runs = (max_kv_len + kKvSplit * kDecodeRun - 1) / (kKvSplit * kDecodeRun);

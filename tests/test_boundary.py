@@ -40,7 +40,9 @@ def test_constants_and_build_id():
     assert bi.gemm_tile() == (256, 256, 64)
     # narrow bf16 weights get 192-wide column tiles; int4 weights and wide ones 256
     assert [bi.gemm_tile_cols(n) for n in (8, 768, 2560, 3072, 3080, 4096, 24576)] == [192] * 4 + [256] * 3
-    assert bi.gemm_tile_cols(2560, int4_weights=True) == 256 and bi.gemm_tile_cols(0) == 0
+    # int4 weights: 192-wide tiles up to 4096 rows
+    assert [bi.gemm_tile_cols(n, int4_weights=True) for n in (8, 2560, 4096, 4104, 6144)] == [192] * 3 + [256] * 2
+    assert bi.gemm_tile_cols(0) == 0
     bid = bi.build_id()
     assert re.fullmatch(r"[0-9a-f]{16}", bid)
     for code in range(7):
