@@ -12,14 +12,15 @@
 //    into halves of 32 keys with one online softmax per half, merged at the
 //    end; half 1 of the diagonal block is skipped when t % 64 < 32 (prefill's
 //    wave for positions 64 j .. 64 j + 31 skips it);
-//  * per key, the D-long score as MFMA steps of 8 dims in ascending order
+//  * per key, the D-long score S as MFMA steps of 8 dims in ascending order
 //    (v_mfma_f32_16x16x32_bf16 here, keys as rows and the G heads as columns;
-//    prefill's v_mfma_f32_32x32x16_bf16 chains the same steps), times
-//    scale * log2(e), keys after t set to -inf;
-//  * within a half, key 4 j + c is of class c: the block maximum, the lazy
-//    rescale (the reference maximum m moves only when the block maximum
-//    exceeds it by more than 8), alpha = exp2(m - m_new),
-//    P = exp2(S - m_new), rowsum = (sum c0 + sum c2) + (sum c1 + sum c3) with
+//    prefill's v_mfma_f32_32x32x16_bf16 chains the same steps), keys after t
+//    set to -inf;
+//  * within a half, key 4 j + c is of class c: the block maximum of S times
+//    scale = softmax scale * log2(e), the lazy rescale (the reference maximum
+//    m moves only when the block maximum exceeds it by more than 8),
+//    alpha = exp2(m - m_new), P = exp2(fma(S, scale, -m_new)),
+//    rowsum = (sum c0 + sum c2) + (sum c1 + sum c3) with
 //    each class summed in ascending j, l = fma(l, alpha, rowsum), O *= alpha;
 //  * P V with P = hi + lo in bf16, the 8-key groups added in the order
 //    hi c0, hi c1, hi c2, hi c3, lo c0, lo c1, lo c2, lo c3;
@@ -212,18 +213,19 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float v = sacc[j >> 2][j & 3] * sscale;
+        float v = sacc[j >> 2][j & 3];
         if (diag && key0 + 4 * j > t) v = -INFINITY;
         p[j] = v;
         mx = fmaxf(mx, v);
       }
-      mx = max_x32(max_x16(mx));
+      // the largest scaled score: scaling by a positive constant keeps the order
+      mx = max_x32(max_x16(mx)) * sscale;
       const bool lift = mx > m_run + 8.0f;
       const float m_new = lift ? mx : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(p[j] - m_new);
+      for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(p[j], sscale, -m_new));
       float cs = p[0];
 #pragma unroll
       for (int j = 1; j < 8; ++j) cs += p[j];

@@ -30,9 +30,10 @@
 //                         rows permuted so that output register r of lane
 //                         half hf holds class 2 (r / 8) + hf, j = r % 8;
 //                         B = Q held in registers), D/16 steps ascending;
-//   the row's reference maximum m moves to rowmax S only when that exceeds
-//   m by more than 8 (log2 units), so weights stay <= 2^8 and O is rescaled
-//   rarely: alpha = exp2(m - m_new), P = exp2(S - m_new) in fp32,
+//   the row's reference maximum m moves to rowmax(S) * scale only when that
+//   exceeds m by more than 8 (log2 units), so weights stay <= 2^8 and O is
+//   rescaled rarely: alpha = exp2(m - m_new), P = exp2(fma(S, scale, -m_new))
+//   in fp32 (one rounding of the scaled, shifted score),
 //   rowsum(P) = ((sum c0 + sum c2) + (sum c1 + sum c3)), each class summed in
 //   ascending j, l = fma(l, alpha, rowsum);
 //   O^T = O^T * alpha + V^T P^T with the same MFMA (A = V^T from a transposed
@@ -41,7 +42,7 @@
 //   1, P_hi of 2 and 3, P_lo of 0 and 1, P_lo of 2 and 3 (each instruction
 //   adds two 8-key groups in order).  Each decision is the row's own, so it
 //   depends on nothing outside the query's keys.
-// Scores are in log2 units (scale * log2(e) applied to S in fp32).  Merge:
+// Scores are in log2 units (scale = softmax scale * log2(e), applied in fp32).  Merge:
 // M = max(m0, m1), a_i = exp2(m_i - M), output
 // bf16(fma(O0, a0, O1 a1) / fma(l0, a0, l1 a1)).
 //
@@ -335,8 +336,6 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         const bool diag = blk == wave_last_blk;
         const int qpos = wpos + l32;
         float mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] *= sscale;
         if (diag) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -346,7 +345,8 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // the largest scaled score: scaling by a positive constant keeps the order
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sscale;
         // the row's reference maximum moves only when the block's maximum
         // exceeds it by more than 8 (log2 units): weights stay <= 2^8
         const bool lift = mx > m_run + 8.0f;
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(NTH, 1) void prefill_kernel(
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] - m_new);
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], sscale, -m_new));
         // per class in ascending j, then (c0 + c2) + (c1 + c3)
         float sa = s[0], sb = s[8];
 #pragma unroll

@@ -36,8 +36,12 @@ __device__ __forceinline__ float bf2f_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint16_t f2bf(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
+// Two values in one v_cvt_pk_bf16_f32 (the same rounding as f2bf on each).
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Unpack 8 bf16 (one 16-byte chunk) into fp32.

@@ -92,14 +92,6 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 }
 
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-
-// Two fp32 values -> packed bf16 pair (one v_cvt_pk_bf16_f32), round to nearest even.
-__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // De-quantise 8 int4 codes (one little-endian word; nibble e is element e) with the
 // group's scale s: w_e = bf16(code_e * s), code_e the two's-complement nibble.  Each
@@ -118,7 +110,7 @@ __device__ __forceinline__ uint4 dequant8(uint32_t word, float sc, float nb) {
     f[j] = __builtin_fmaf(float(p[0]), sc, nb);
     f[j + 4] = __builtin_fmaf(float(p[1]), sc, nb);
   }
-  return make_uint4(pk_bf16(f[0], f[1]), pk_bf16(f[2], f[3]), pk_bf16(f[4], f[5]), pk_bf16(f[6], f[7]));
+  return make_uint4(pack2bf(f[0], f[1]), pack2bf(f[2], f[3]), pack2bf(f[4], f[5]), pack2bf(f[6], f[7]));
 }
 
 // Expand one int4 group (16 bytes = 32 codes, one fp16 scale) into four bf16 16-byte
