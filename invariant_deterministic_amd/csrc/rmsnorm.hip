@@ -10,7 +10,8 @@
 //   it accumulates x^2 with fmaf over its chunks in ascending c, and within a
 //   chunk over its 8 elements in ascending order; the 64 lane partials are
 //   then combined by a fixed xor butterfly (32, 16, 8, 4, 2, 1).
-// The row is read from HBM once and kept in registers for the scaling pass.
+// The row is read from HBM once and kept in registers for the scaling pass;
+// loads and stores stream past the caches (each byte is touched once).
 #include "bi_dev.h"
 #include "bi_internal.h"
 
@@ -54,7 +55,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint4* __restrict__ 
       unpack8(gamma[c], g);
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = (f[e] * r) * g[e];
-      yr[c] = pack8(f);
+      const uint4 r4 = pack8(f);
+      const u32x4 rv = {r4.x, r4.y, r4.z, r4.w};
+      __builtin_nontemporal_store(rv, reinterpret_cast<u32x4*>(yr + c));
     }
   }
 }
