@@ -217,7 +217,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
 
   // ---- global load assignment
   // A tile: 256 rows x 8 chunks; thread t loads chunk (t & 7) of rows (t >> 3) + 64 i.
-  // W tile: thread t expands the 32-code group t & 1 of tile row t >> 1.  A 192-wide tile
+  // W tile: thread t expands the 32-code group t & 1 of tile row q_row.  A 192-wide tile
   // uses rows 0 .. 191 of the LDS tile; the threads of rows 192 .. 255 expand a clamped row
   // into the unused rest (no branch in the loop).
   // Rows past M (past N for W) are clamped: computed, never stored.
@@ -227,7 +227,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
   const uint16_t* a_base = A + ld_chunk * 8;
   int a_r0 = min(tm * BM + ld_row, a_last), a_r1 = min(tm * BM + ld_row + 64, a_last);
   int a_r2 = min(tm * BM + ld_row + 128, a_last), a_r3 = min(tm * BM + ld_row + 192, a_last);
-  const int q_row = t >> 1;
+  // Each 8-lane group of a wave writes 4 rows whose swizzle keys (row / 2) % 8 are
+  // 4 a + 0..3 (rows 8 a + p, + 2, + 4, + 6), both halves each: the 8 lanes' 16-byte chunks
+  // of one write instruction land on 8 distinct chunk positions (no bank conflict).
+  const int q_row = 8 * (t >> 4) + 2 * ((t >> 1) & 3) + ((t >> 3) & 1);
   const int q_half = t & 1;
   const int q_r = min(w_row<EPI, BNT>(tn, q_row, N), w_last);
   const uint8_t* q_src = Wq + int64_t(q_r) * (K / 2) + q_half * 16;
