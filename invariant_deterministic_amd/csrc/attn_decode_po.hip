@@ -47,12 +47,12 @@ constexpr int KB = kPrefillKeyBlock;  // 64 keys per block
 constexpr int NT = 128;               // two waves
 
 template <int D, int G, bool Q8>
-__global__ __launch_bounds__(NT) void decode_po_kernel(
+__device__ __forceinline__ void decode_po_body(
     const uint16_t* __restrict__ q, int64_t q_stride, const void* __restrict__ k_all,
     const void* __restrict__ v_all, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
     const int32_t* __restrict__ block_tables, int max_pages, int64_t n_pages, const DecodeSeq* __restrict__ seqs,
     const int64_t* __restrict__ kv_offset, const int32_t* __restrict__ kv_len,
-    const int32_t* __restrict__ order, int Hkv, int64_t max_len, float sscale,
+    const int32_t* __restrict__ order, int B, int Hkv, int64_t max_len, float sscale,
     uint16_t* __restrict__ o, int64_t o_stride) {
   constexpr int LD = D / 16;  // dims per lane in the token-major loads
   constexpr int NDW = LD / 2;
@@ -64,8 +64,14 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
   __shared__ float s_o[G * D];    // half 1's O
   __shared__ float s_ml[2][2][G];  // [half][m, l][head]
 
-  const int g = blockIdx.x;
-  const int b = order ? order[blockIdx.y] : int(blockIdx.y);
+  // Grid (8 Hkv, ceil(B / 8)): work-group w = x + 8 Hkv y runs on XCD w % 8 = x % 8, and
+  // takes kv head x / 8 of request slot 8 y + x % 8, so the kv heads of one request run
+  // together on one XCD and share its L2 (the int8 cache's per-token scales of all heads
+  // sit in one 32-byte sector).  Slots past B do nothing.
+  const int g = int(blockIdx.x) >> 3;
+  const int slot = int(blockIdx.y) * 8 + (int(blockIdx.x) & 7);
+  if (slot >= B) return;
+  const int b = order ? order[slot] : slot;
   // koff: cache row of key 0 (bf16); pt: first page-table entry of the request (int8 cache,
   // addressed through page tables: the sequence's kv_offset in one flat table, or row b of
   // per-request tables [B, max_pages])
@@ -175,12 +181,15 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
   uint16_t* sk = s_k[kh];
   const int rr = 4 * (l16 & 3) + (l16 >> 2);  // K tile row read as MFMA row l16
 
-  // per block: scores, online softmax and value product of this wave's half
+  // per block, in two stages: scores (K tile through LDS, S = K Q^T on MFMA), then the
+  // online softmax and value product of this wave's half.  The int8 loop runs the scores
+  // of block j + 1 beside the softmax and P V of block j (independent work the scheduler
+  // can interleave), with three register sets in rotation so block j + 2's loads are in
+  // flight meanwhile.  Every block's operations and their order are the same either way.
   // kword(it, c): dword c (two bf16) of key it's K slice; vpair(jj, e): dim e of keys 2 jj, 2 jj + 1
-  auto process = [&](auto&& kword, auto&& vpair, int blk) {
+  auto scores = [&](auto&& kword, f32x4 (&sacc)[2]) {
       // ---- scores: two 16-key tiles; tile row 4 j + grp holds key 4 (4 kb + j) + grp, so
       // output register r of lane (head l16, grp) is key 4 (4 kb + r) + grp
-      f32x4 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -206,6 +215,8 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
           sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(qq), sacc[kb], 0, 0, 0);
         }
       }
+  };
+  auto soft_pv = [&](const f32x4 (&sacc)[2], auto&& vpair, int blk) {
       // ---- online softmax of this half (lane: head l16, class grp, j = 4 kb + r)
       const bool diag = blk == nblk - 1;
       const int key0 = blk * KB + 32 * kh + grp;
@@ -261,11 +272,15 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
       }
   };
 
-  // two register sets, alternating, so the next block's loads are in flight
-  // while a block is processed (past the request's keys the loads read zeros)
+  // past the request's keys the loads read zeros (bf16) or nothing (int8); the int8 loop
+  // computes the scores of the block after the last and never uses them
   if constexpr (!Q8) {
+    // bf16: two register sets, alternating, each block's scores then its softmax and P V
+    uint32_t kw[8][NDW], vw[8][NDW], nkw[8][NDW], nvw[8][NDW];
     auto run = [&](const uint32_t (&kd)[8][NDW], const uint32_t (&vd)[8][NDW], int blk) {
-      process([&](int it, int c) { return kd[it][c]; },
+      f32x4 sa[2];
+      scores([&](int it, int c) { return kd[it][c]; }, sa);
+      soft_pv(sa,
               [&](int jj, int e) {
                 return __builtin_amdgcn_perm(vd[2 * jj + 1][e >> 1], vd[2 * jj][e >> 1],
                                              (e & 1) ? 0x07060302u : 0x05040100u);
@@ -283,32 +298,49 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
   } else {
     // int8 codes dequantised where they are consumed: K while the K tile is written, V while
     // the value operand is built (the same bf16(float(code) * scale) values throughout)
-    auto run_q = [&](const uint32_t (&kd)[8][NQ], float ksr, const uint32_t (&vd)[8][NQ], float vsr, int blk) {
-      float ks[8], vs[8];
+    uint32_t k0[8][NQ], v0[8][NQ], k1[8][NQ], v1[8][NQ], k2[8][NQ], v2[8][NQ];
+    float ks0 = 0.f, vs0 = 0.f, ks1 = 0.f, vs1 = 0.f, ks2 = 0.f, vs2 = 0.f;
+    f32x4 s0[2], s1[2], s2[2];
+    auto sc = [&](const uint32_t (&kd)[8][NQ], float ksr, f32x4 (&sa)[2]) {
+      float ks[8];
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        ks[it] = __shfl(ksr, 4 * it + grp, 64);
-        vs[it] = __shfl(vsr, 4 * it + grp, 64);
-      }
-      process([&](int it, int c) {
-                const uint32_t w = kd[it][c >> 1];
-                const int b0 = 2 * (c & 1);
-                return pack2bf(dq(w, b0, ks[it]), dq(w, b0 + 1, ks[it]));
-              },
+      for (int it = 0; it < 8; ++it) ks[it] = __shfl(ksr, 4 * it + grp, 64);
+      scores([&](int it, int c) {
+               const uint32_t w = kd[it][c >> 1];
+               const int b0 = 2 * (c & 1);
+               return pack2bf(dq(w, b0, ks[it]), dq(w, b0 + 1, ks[it]));
+             },
+             sa);
+    };
+    auto sp = [&](const f32x4 (&sa)[2], const uint32_t (&vd)[8][NQ], float vsr, int blk) {
+      float vs[8];
+#pragma unroll
+      for (int it = 0; it < 8; ++it) vs[it] = __shfl(vsr, 4 * it + grp, 64);
+      soft_pv(sa,
               [&](int jj, int e) {
-                return pack2bf(dq(vd[2 * jj][e >> 2], e & 3, vs[2 * jj]), dq(vd[2 * jj + 1][e >> 2], e & 3, vs[2 * jj + 1]));
+                return pack2bf(dq(vd[2 * jj][e >> 2], e & 3, vs[2 * jj]),
+                               dq(vd[2 * jj + 1][e >> 2], e & 3, vs[2 * jj + 1]));
               },
               blk);
     };
-    uint32_t kq[8][NQ], vq[8][NQ], nkq[8][NQ], nvq[8][NQ];
-    float ksr = 0.f, vsr = 0.f, nksr = 0.f, nvsr = 0.f;
-    if (nb > 0) load_q(kq, ksr, vq, vsr, 0);
-    for (int blk = 0; blk < nb; blk += 2) {
-      load_q(nkq, nksr, nvq, nvsr, blk + 1);
-      run_q(kq, ksr, vq, vsr, blk);
-      if (blk + 1 >= nb) break;
-      load_q(kq, ksr, vq, vsr, blk + 2);
-      run_q(nkq, nksr, nvq, nvsr, blk + 1);
+    if (nb > 0) {
+      load_q(k0, ks0, v0, vs0, 0);
+      load_q(k1, ks1, v1, vs1, 1);
+      sc(k0, ks0, s0);
+      for (int blk = 0;; blk += 3) {
+        load_q(k2, ks2, v2, vs2, blk + 2);
+        sc(k1, ks1, s1);
+        sp(s0, v0, vs0, blk);
+        if (blk + 1 >= nb) break;
+        load_q(k0, ks0, v0, vs0, blk + 3);
+        sc(k2, ks2, s2);
+        sp(s1, v1, vs1, blk + 1);
+        if (blk + 2 >= nb) break;
+        load_q(k1, ks1, v1, vs1, blk + 4);
+        sc(k0, ks0, s0);
+        sp(s2, v2, vs2, blk + 2);
+        if (blk + 3 >= nb) break;
+      }
     }
   }
 
@@ -351,13 +383,46 @@ __global__ __launch_bounds__(NT) void decode_po_kernel(
   }
 }
 
+#define BI_DPO_PARAMS                                                                                     \
+  const uint16_t *__restrict__ q, int64_t q_stride, const void *__restrict__ k_all,                         \
+      const void *__restrict__ v_all, const float *__restrict__ k_scale, const float *__restrict__ v_scale,  \
+      const int32_t *__restrict__ block_tables, int max_pages, int64_t n_pages,                             \
+      const DecodeSeq *__restrict__ seqs, const int64_t *__restrict__ kv_offset,                            \
+      const int32_t *__restrict__ kv_len, const int32_t *__restrict__ order, int B, int Hkv,                \
+      int64_t max_len, float sscale, uint16_t *__restrict__ o, int64_t o_stride
+#define BI_DPO_ARGS                                                                                       \
+  q, q_stride, k_all, v_all, k_scale, v_scale, block_tables, max_pages, n_pages, seqs, kv_offset, kv_len,   \
+      order, B, Hkv, max_len, sscale, o, o_stride
+
+template <int D, int G>
+__global__ __launch_bounds__(NT) void decode_po_kernel(BI_DPO_PARAMS) {
+  decode_po_body<D, G, false>(BI_DPO_ARGS);
+}
+
+// The int8 kernel is held to two waves per SIMD (at most 256 registers): left free, the
+// compiler takes over 300 for the three rotating register sets and runs one wave per SIMD,
+// about a quarter slower; at two waves it needs no spills.
+template <int D, int G>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_po_q8_kernel(
+    BI_DPO_PARAMS) {
+  decode_po_body<D, G, true>(BI_DPO_ARGS);
+}
+#undef BI_DPO_PARAMS
+#undef BI_DPO_ARGS
+
 template <int D, int G, bool Q8>
 hipError_t launch_t(const uint16_t* q, int64_t q_stride, const void* k_all, const void* v_all, const float* ks,
                     const float* vs, const int32_t* bt, int max_pages, int64_t n_pages, const DecodeSeq* seqs,
                     const int64_t* kv_offset, const int32_t* kv_len, const int32_t* order, int B, int64_t max_len,
                     int Hkv, float sscale, uint16_t* o, int64_t o_stride, hipStream_t s) {
-  hipLaunchKernelGGL((decode_po_kernel<D, G, Q8>), dim3(Hkv, B), dim3(NT), 0, s, q, q_stride, k_all, v_all, ks, vs, bt,
-                     max_pages, n_pages, seqs, kv_offset, kv_len, order, Hkv, max_len, sscale, o, o_stride);
+  if (B <= 0) return hipSuccess;
+  const dim3 grid(8 * Hkv, (B + 7) / 8);
+  if constexpr (Q8)
+    hipLaunchKernelGGL((decode_po_q8_kernel<D, G>), grid, dim3(NT), 0, s, q, q_stride, k_all, v_all, ks, vs, bt,
+                       max_pages, n_pages, seqs, kv_offset, kv_len, order, B, Hkv, max_len, sscale, o, o_stride);
+  else
+    hipLaunchKernelGGL((decode_po_kernel<D, G>), grid, dim3(NT), 0, s, q, q_stride, k_all, v_all, ks, vs, bt,
+                       max_pages, n_pages, seqs, kv_offset, kv_len, order, B, Hkv, max_len, sscale, o, o_stride);
   return hipGetLastError();
 }
 
