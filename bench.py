@@ -48,19 +48,30 @@ def parse():
 
 
 # --------------------------------------------------------------- helpers
-def event_time_ms(torch, fn, reps):
-    """Average duration of fn() (kernels on torch's current stream) with HIP events."""
+def event_time_ms(torch, fn, reps, warm_ms=30.0, groups=3):
+    """Average duration of fn() (kernels on torch's current stream) with HIP events: after
+    at least warm_ms of back-to-back warm-up calls (the clock needs a few milliseconds of
+    load to reach its working frequency after the host has left the GPU idle), `groups`
+    groups of `reps` back-to-back calls are timed; the median group's average is returned."""
     s = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    fn()
-    torch.cuda.synchronize()
     start.record(s)
-    for _ in range(reps):
-        fn()
+    fn()
     end.record(s)
     end.synchronize()
-    return start.elapsed_time(end) / reps
+    first = max(start.elapsed_time(end), 1e-3)
+    for _ in range(min(2000, int(math.ceil(warm_ms / first)))):
+        fn()
+    avg = []
+    for _ in range(groups):
+        start.record(s)
+        for _ in range(reps):
+            fn()
+        end.record(s)
+        end.synchronize()
+        avg.append(start.elapsed_time(end) / reps)
+    return sorted(avg)[groups // 2]
 
 
 def time_steps(torch, step, steps, warmup):
@@ -72,6 +83,32 @@ def time_steps(torch, step, steps, warmup):
         step()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) / steps * 1e3
+
+
+def step_event_stats(torch, step, n):
+    """Per-step HIP-event durations of n more steps (after the contract's timed region):
+    median, min and max in ms, each step bracketed by its own pair of events."""
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(s)
+        step()
+        b.record(s)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"median": ts[n // 2] if n % 2 else 0.5 * (ts[n // 2 - 1] + ts[n // 2]), "min": ts[0], "max": ts[-1],
+            "n": n}
+
+
+def copy_ceiling_gbs(torch):
+    """HBM rate of torch's plain 1 GiB device-to-device copy (bytes read + written / time):
+    what a generic streaming kernel reaches on this device, beside the 8 TB/s peak."""
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    t = event_time_ms(torch, lambda: dst.copy_(src), 10)
+    del src, dst
+    return 2.0 * n * 2 / t / 1e6
 
 
 def cpu_cores():
@@ -161,6 +198,7 @@ def run_mixed(args, torch, bi, synth):
         blk.forward(x, seqs, kp, vp, y=y, ws=ws, meta=meta)
 
     ms = time_steps(torch, step, args.steps, args.warmup)
+    per_step = step_event_stats(torch, step, max(args.steps, 5))
     tokens = args.batch + 2048
     # the same step with the other decode order (same weights, cache and inputs)
     other = "split" if po else "prefill"
@@ -204,6 +242,9 @@ def run_mixed(args, torch, bi, synth):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = recorded_traffic(roof)
     roof["kernel_ms"] = t_dec if roof["bound"] == "hbm" else t_gu
+    copy_gbs = copy_ceiling_gbs(torch)
+    if roof["bound"] == "hbm":
+        roof["frac_of_torch_copy"] = roof["achieved"] / copy_gbs
 
     out = {
         "metric": "batch-invariant block tokens/s",
@@ -211,6 +252,7 @@ def run_mixed(args, torch, bi, synth):
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "per_step_ms": per_step, "torch_copy_gbs": copy_gbs,
         "dtype": "bf16 activations, int4 weights, fp32 accumulation", "data": "synthetic (seeded)",
         "config": {"workload": "int4 block hidden 4096, FFN 12288, 32/8 heads x 128: mixed step of "
                                f"{args.batch} decodes (KV 512..8192) + one 2048-token prefill chunk",
@@ -313,15 +355,21 @@ def run_decode(args, torch, bi, synth):
 
 
 def run_norm(args, torch, bi, synth):
-    M, H = 65536, 4096
-    x = synth.normal_bf16_device(1200, (M, H))
-    g = bi.to_dev(synth.normal_bf16(1201, (H,), 0.02, 1.0))
-    y = torch.empty_like(x)
-    t = event_time_ms(torch, lambda: bi.rmsnorm(x, g, 1e-6, out=y), max(args.kernel_reps, 20))
-    by = 2.0 * M * H * 2
-    return {"metric": "RMSNorm GB/s", "value": by / t / 1e6, "unit": "GB/s", "ms": t,
-            "frac": by / t / 1e6 / (PEAK_HBM / 1e9), "config": {"workload": "65536 x 4096"},
-            "build_id": bi.build_id()}
+    """RMSNorm at 65536 x 4096 (the value), and at the blocks' own shapes: the int4 mixed
+    step (2304 x 4096) and the dense block's 4000-token prefill (4000 x 2560)."""
+    res = {}
+    for M, H in ((65536, 4096), (2304, 4096), (4000, 2560)):
+        x = synth.normal_bf16_device(1200 + H, (M, H))
+        g = bi.to_dev(synth.normal_bf16(1201, (H,), 0.02, 1.0))
+        y = torch.empty_like(x)
+        t = event_time_ms(torch, lambda: bi.rmsnorm(x, g, 1e-6, out=y), max(args.kernel_reps, 20))
+        by = 2.0 * M * H * 2
+        res[f"{M}x{H}"] = {"ms": t, "gbs": by / t / 1e6, "frac": by / t / 1e6 / (PEAK_HBM / 1e9)}
+        del x, y
+    big = res["65536x4096"]
+    return {"metric": "RMSNorm GB/s", "value": big["gbs"], "unit": "GB/s", "ms": big["ms"], "frac": big["frac"],
+            "config": {"workload": "65536 x 4096 (value); 2304 x 4096 and 4000 x 2560 beside it"},
+            "shapes": res, "torch_copy_gbs": copy_ceiling_gbs(torch), "build_id": bi.build_id()}
 
 
 def run_dense(args, torch, bi, synth):
