@@ -42,16 +42,18 @@
 // 8-byte write.
 //
 // bf16 weights use a second schedule with the same per-element MFMA chain (so
-// the same bits): the eight waves form two groups of four, one
-// wave of each group per SIMD, that take turns -- while one group issues the
-// 16 MFMAs of half a stage from registers, the other reads its next
-// half-stage's fragments from LDS -- separated by work-group barriers, group 1
-// one barrier behind group 0.  Both operand tiles go from global memory
+// the same bits): four waves, one per SIMD, each owning a 128 x BNT/2 block of
+// the tile (256 accumulator registers): 0.5 LDS fragment reads per MFMA against
+// 0.75 for eight 64-row waves.  Both operand tiles go from global memory
 // straight into LDS (global_load_lds_dwordx4, no staging registers), a stage
 // ahead, each LDS stage a separate array so the compiler can tell the pending
-// loads from the reads.  Operand offsets are 32-bit and relative to the tile's
-// first rows, so one schedule serves every operand size.
+// loads from the reads.  The wave issues, between the MFMAs of each 16-deep
+// substep, the next substep's fragment reads and the next stage's direct loads
+// in a fixed interleaved order: issued in one burst, the loads held up the
+// in-order MFMA stream behind them.  Operand offsets are 32-bit and relative to
+// the tile's first rows, so one schedule serves every operand size.
 #include <type_traits>
+#include <utility>
 
 #include "bi_dev.h"
 #include "bi_internal.h"
@@ -60,7 +62,8 @@ namespace bi {
 namespace {
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int NT = 512;                 // 8 waves: 2 along N (half the tile width each) x 4 along M (64 each)
+constexpr int NT = 512;                 // int4: 8 waves, 2 along N (half the tile width each) x 4 along M (64 each)
+constexpr int NT4 = 256;                // bf16: 4 waves, 2 along N x 2 along M (128 each), one per SIMD
 constexpr int TILE = BM * BK;           // bf16 elements of one operand tile (BM == BN)
 constexpr int kStoreAfter = 2;         // the next stage is written to LDS after this substep's MFMAs
 static_assert(BM == BN, "square tile assumed by the LDS layout");
@@ -141,17 +144,17 @@ __device__ __forceinline__ int w_row(int tn, int t, int F) {
   else return tn * BNT + t;
 }
 
-// acc[bn][bm][r] is tile element (row wm*64 + bm*32 + (lane & 31), column wn*(BNT/2) + bn*32 +
-// 8*(r/4) + 4*(lane/32) + r%4) of a BM x BNT tile; C has N columns (the gated form: N = F
-// outputs, BNT = 256)
-template <int EPI, int BNT>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BNT / 64][2], uint16_t* C,
-                                           const uint16_t* R, int M, int N, int tm, int tn,
-                                           int wm, int wn, int lane) {
+// acc[bn][bm][r] is C element (row row0 + bm*32 + (lane & 31), column tn*BNT + wn*(BNT/2) +
+// bn*32 + 8*(r/4) + 4*(lane/32) + r%4) of a wave's NBR 32-row blocks of a BM x BNT tile; C has
+// N columns (the gated form: N = F outputs, BNT = 256)
+template <int EPI, int BNT, int NBR>
+__device__ __forceinline__ void store_rows(const f32x16 (&acc)[BNT / 64][NBR], uint16_t* C,
+                                           const uint16_t* R, int M, int N, int row0, int tn,
+                                           int wn, int lane) {
   static_assert(EPI != kEpiGated || BNT == 256, "the gated epilogue pairs 128-column halves of a 256 tile");
 #pragma unroll
-  for (int bm = 0; bm < 2; ++bm) {
-    const int m = tm * BM + wm * 64 + bm * 32 + (lane & 31);
+  for (int bm = 0; bm < NBR; ++bm) {
+    const int m = row0 + bm * 32 + (lane & 31);
     if (m >= M) continue;
     uint16_t* crow = C + int64_t(m) * N;
     if constexpr (EPI == kEpiGated) {
@@ -191,6 +194,14 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[BNT / 64][2], uin
       }
     }
   }
+}
+
+// the int4 kernel's waves: two 32-row blocks at tile rows wm*64 ..
+template <int EPI, int BNT>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BNT / 64][2], uint16_t* C,
+                                           const uint16_t* R, int M, int N, int tm, int tn,
+                                           int wm, int wn, int lane) {
+  store_rows<EPI, BNT, 2>(acc, C, R, M, N, tm * BM + wm * 64, tn, wn, lane);
 }
 
 // int4-weight GEMM, register-staged schedule (see the file comment), BM x BNT x BK tiles.
@@ -352,14 +363,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restri
 #undef BI_STORE_LDS
 }
 
-// s_waitcnt immediates (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr unsigned kWaitVm0 = 0x0F70;    // vmcnt(0)
-constexpr unsigned kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
-
-// A work-group barrier that orders the compiler's memory operations but is no memory
-// fence: the schedule below waits for LDS reads (lgkmcnt) and direct loads (vmcnt)
-// itself, exactly where it needs them, so later loads stay in flight across barriers.
-__device__ __forceinline__ void ping_pong_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// s_waitcnt immediate (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr unsigned kWaitVm0 = 0x0F70;  // vmcnt(0)
 
 // One 16-byte-per-lane direct load into LDS: lane l's 16 bytes from src land at dst + 16 l
 // bytes (dst wave-uniform).  A plain function, so that calls from templates whose
@@ -368,19 +373,40 @@ __device__ __forceinline__ void load_lds_b128(const char* src, uint16_t* dst) {
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
 }
 
-// bf16 GEMM, ping-pong schedule (see the file comment), BM x BNT x BK tiles (BNT = 256, or
-// 192 for narrow weights).  Operand offsets are 32-bit byte offsets from the tile's first
-// row of A and of W (the caller checks (BM + 1) K 2 < 2^32, and for the gated form
-// (F + 256) K 2 < 2^32).
+// The extra instructions issued after MFMA i of a 16-deep substep: the substep's list of
+// nr fragment reads (for the next substep) and nd direct loads (of the next stage), merged
+// read, load, read, load, ... (the longer list's rest at the end), is spread evenly over its
+// nm MFMAs: MFMA i is followed by list entries first(i) .. first(i + 1) - 1.
+constexpr int issue_first(int i, int nops, int nm) { return i * nops / nm; }
+// entry q of the merged list: kind (0 read, 1 load) and index within its own list
+constexpr int issue_kind(int q, int nr, int nd) { return q < 2 * (nr < nd ? nr : nd) ? (q & 1) : (nr > nd ? 0 : 1); }
+constexpr int issue_index(int q, int nr, int nd) {
+  return q < 2 * (nr < nd ? nr : nd) ? (q >> 1) : q - (nr < nd ? nr : nd);
+}
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), in order
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// bf16 GEMM (see the file comment), BM x BNT x BK tiles, four waves of 128 x BNT/2.  Operand
+// offsets are 32-bit byte offsets from the tile's first row of A and of W (the caller checks
+// (BM + 1) K 2 < 2^32, and for the gated form (F + 256) K 2 < 2^32).
 template <int EPI, int BNT>
-__global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restrict__ A,
-                                                        const uint16_t* __restrict__ W,
-                                                        const uint16_t* R,  // may alias C (resid)
-                                                        uint16_t* C, int M, int N, int K,
-                                                        int tiles_n, int n_tiles) {
+__global__ __launch_bounds__(NT4, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ A,
+                                                           const uint16_t* __restrict__ W,
+                                                           const uint16_t* R,  // may alias C (resid)
+                                                           uint16_t* C, int M, int N, int K,
+                                                           int tiles_n, int n_tiles) {
   static_assert(BNT == 256 || (BNT == 192 && EPI != kEpiGated), "tile width");
-  constexpr int NB = BNT / 64;        // 32-column blocks per wave (two waves along N)
-  constexpr int WB = BNT / 64;        // 1 KB blocks of the W tile each wave loads
+  constexpr int NB = BNT / 64;   // 32-column blocks per wave (two waves along N)
+  constexpr int WB = BNT / 32;   // 1 KB blocks of the W tile each wave loads
+  constexpr int NM = NB * 4;     // MFMAs per 16-deep substep
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sW0[BNT * BK];
@@ -389,17 +415,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
   const int tile = tile_of(blockIdx.x, n_tiles, tiles_n);
   const int tm = tile / tiles_n;
   const int tn = tile % tiles_n;
-
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = int(__builtin_amdgcn_readfirstlane(t >> 6));
-  const int gp = wave >> 2;           // wave group; wave w runs on SIMD w % 4
-  const int s4 = wave & 3;
-  const int wn = s4 & 1;              // BNT / 2 output columns
-  const int wm = (s4 >> 1) + 2 * gp;  // 64 output rows
+  const int wn = wave & 1;   // BNT / 2 output columns
+  const int wm = wave >> 1;  // 128 output rows
 
-  // Direct loads: wave w fills 1 KB blocks 4w .. 4w + 3 of the A tile (rows 32w .. 32w +
-  // 31) and blocks WB w .. WB w + WB - 1 of the W tile; lane l writes bytes 16 l of its
+  // Direct loads: wave w fills 1 KB blocks 8w .. 8w + 7 of the A tile (rows 64w .. 64w +
+  // 63) and blocks WB w .. WB w + WB - 1 of the W tile; lane l writes bytes 16 l of its
   // block: tile row 8 b + l / 8, stored chunk l % 8, which holds logical chunk
   // (l % 8) ^ ((row / 2) % 8) (the layout lds_off describes).  Rows past M (past N) are
   // clamped: computed, never stored.
@@ -408,10 +431,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
   const uint16_t* Wt = W + int64_t(w_first) * K;
   const int a_rows = min(BM, M - tm * BM);
   const int w_last = (EPI == kEpiGated ? 2 * N : N) - 1;
-  uint32_t a_vo[4], w_vo[WB];
+  uint32_t a_vo[8], w_vo[WB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 32 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < 8; ++j) {
+    const int row = 64 * wave + 8 * j + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     a_vo[j] = uint32_t(min(row, a_rows - 1)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
   }
@@ -421,21 +444,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
     w_vo[j] = uint32_t(min(w_row<EPI, BNT>(tn, row, N), w_last) - w_first) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
   }
-  auto issue_loads = [&](int kt, uint16_t* dA, uint16_t* dW) {
-    const char* Ab = reinterpret_cast<const char*>(At + kt * BK);
-    const char* Wb = reinterpret_cast<const char*>(Wt + kt * BK);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) load_lds_b128(Ab + a_vo[j], dA + (4 * wave + j) * 512);
-#pragma unroll
-    for (int j = 0; j < WB; ++j)
-      load_lds_b128(Wb + w_vo[j], dW + (WB * wave + j) * 512);
+  auto load_a = [&](int kt, uint16_t* dA, int j) {
+    load_lds_b128(reinterpret_cast<const char*>(At + kt * BK) + a_vo[j], dA + (8 * wave + j) * 512);
+  };
+  auto load_w = [&](int kt, uint16_t* dW, int j) {
+    load_lds_b128(reinterpret_cast<const char*>(Wt + kt * BK) + w_vo[j], dW + (WB * wave + j) * 512);
   };
 
-  f32x16 acc[NB][2];
+  f32x16 acc[NB][4];
 #pragma unroll
   for (int bn = 0; bn < NB; ++bn)
 #pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
+    for (int bm = 0; bm < 4; ++bm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[bn][bm][r] = 0.f;
 
@@ -443,71 +463,91 @@ __global__ __launch_bounds__(NT, 1) void gemm_pp_kernel(const uint16_t* __restri
   // ((lane & 31) / 2) % 8: a fragment's LDS offset is (row base) * BK + a lane offset
   const int fr = lane & 31, fc = lane >> 5;
   const int fkey = (fr >> 1) & 7;
-  const int a_base = (wm * 64) * BK, w_base = (wn * (BNT / 2)) * BK;
-  bf16x8 wf[2][NB], af[2][2];
-  auto read_frags = [&](const uint16_t* sA, const uint16_t* sW, int h) {  // k-substeps 2h, 2h + 1
+  const int a_base = (wm * 128) * BK, w_base = (wn * (BNT / 2)) * BK;
+  const int wave_row0 = tm * BM + wm * 128;
+
+  // One K step from stage (sA, sW): four 16-deep substeps of NM MFMAs.  The fragments of
+  // substep kk + 1 are read, and stage kn's direct loads issued (A during substep 0, W
+  // during substep 1; kn < 0: none), between the MFMAs of substep kk in a fixed order, each
+  // MFMA and what follows it fenced from the scheduler.  A wave whose 128 rows all lie past
+  // M (DO = false) only issues its loads: that removes padding work alone.
+  auto step = [&](const uint16_t* sA, const uint16_t* sW, int kn, uint16_t* nA, uint16_t* nW, auto do_c) {
+    if constexpr (!decltype(do_c)::value) {
+      if (kn >= 0) {
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      const int lo = fr * BK + (((2 * (2 * h + k2) + fc) ^ fkey) << 3);
+        for (int j = 0; j < 8; ++j) load_a(kn, nA, j);
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm) af[k2][bm] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo + bm * 32 * BK);
+        for (int j = 0; j < WB; ++j) load_w(kn, nW, j);
+      }
+    } else {
+      bf16x8 wf[2][NB], af[2][4];
+      {
+        const int lo = fr * BK + ((fc ^ fkey) << 3);
 #pragma unroll
-      for (int bn = 0; bn < NB; ++bn) wf[k2][bn] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo + bn * 32 * BK);
+        for (int bm = 0; bm < 4; ++bm) af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo + bm * 32 * BK);
+#pragma unroll
+        for (int bn = 0; bn < NB; ++bn) wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo + bn * 32 * BK);
+      }
+      static_for<BK / 16>([&](auto kk_c) {
+        constexpr int kk = decltype(kk_c)::value;
+        constexpr int cb = kk & 1;
+        constexpr int nr = kk + 1 < BK / 16 ? 4 + NB : 0;
+        constexpr int nd = kk == 0 ? 8 : (kk == 1 ? WB : 0);
+        const int lo_n = fr * BK + (((2 * (kk + 1) + fc) ^ fkey) << 3);
+        static_for<NM>([&](auto i_c) {
+          constexpr int i = decltype(i_c)::value;
+          acc[i >> 2][i & 3] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][i >> 2], af[cb][i & 3], acc[i >> 2][i & 3], 0, 0, 0);
+          constexpr int q0 = issue_first(i, nr + nd, NM);
+          static_for<issue_first(i + 1, nr + nd, NM) - q0>([&](auto d_c) {
+            constexpr int q = q0 + decltype(d_c)::value;
+            constexpr int x = issue_index(q, nr, nd);
+            if constexpr (issue_kind(q, nr, nd) == 0) {
+              if constexpr (x < 4) af[cb ^ 1][x] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo_n + x * 32 * BK);
+              else wf[cb ^ 1][x - 4] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo_n + (x - 4) * 32 * BK);
+            } else {
+              if (kn >= 0) {
+                if constexpr (kk == 0) load_a(kn, nA, x);
+                else load_w(kn, nW, x);
+              }
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
     }
   };
-  // 32-row blocks entirely past M are skipped (padding work only)
-  const int wave_row0 = tm * BM + wm * 64;
-  const int nbm = wave_row0 >= M ? 0 : (wave_row0 + 32 >= M ? 1 : 2);
-  auto mfmas = [&](auto nbm_c) {
-    constexpr int NBM = decltype(nbm_c)::value;
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-      for (int bn = 0; bn < NB; ++bn)
-#pragma unroll
-        for (int bm = 0; bm < NBM; ++bm)
-          acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[k2][bn], af[k2][bm], acc[bn][bm], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
-  };
 
-  // Stage k lives in LDS buffer k % 2.  Iteration k (every wave; group 1 one barrier
-  // later): [issue stage k + 1's loads, read half 0 of stage k] | [MFMAs] | [read half 1,
-  // wait for this wave's stage k + 1 loads] | [MFMAs], each part ending at a barrier.
-  // Stage k + 1's buffer last held stage k - 1, whose last reader (group 1, third part of
-  // iteration k - 1) passed a barrier before group 0 starts iteration k; every wave's
-  // stage k + 1 loads are complete before the barrier after which group 0 reads them.
+  // Stage k lives in LDS buffer k % 2.  Step k: wait for this wave's stage-k loads, barrier
+  // (every wave's stage-k loads have landed and every wave is done reading stage k - 1, whose
+  // buffer stage k + 1 takes), then the step, issuing stage k + 1's loads.  The loop takes
+  // two steps at a time, so the buffers stay compile-time distinct (the compiler can then
+  // tell the loads in flight from the reads); an odd last step follows it.
   const int KT = K / BK;
-  auto run = [&](auto nbm_c) {
-    issue_loads(0, sA0, sW0);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    if (gp == 1) ping_pong_barrier();
-    auto iter = [&](int k, uint16_t* cA, uint16_t* cW, uint16_t* nA, uint16_t* nW) {
-      if (k + 1 < KT) issue_loads(k + 1, nA, nW);
-      read_frags(cA, cW, 0);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      ping_pong_barrier();
-      mfmas(nbm_c);
-      ping_pong_barrier();
-      read_frags(cA, cW, 1);
+  auto run = [&](auto do_c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) load_a(0, sA0, j);
+#pragma unroll
+    for (int j = 0; j < WB; ++j) load_w(0, sW0, j);
+    int k = 0;
+    for (; k + 1 < KT; k += 2) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      ping_pong_barrier();
-      mfmas(nbm_c);
-      ping_pong_barrier();
-    };
-    for (int k = 0; k < KT; k += 2) {
-      iter(k, sA0, sW0, sA1, sW1);
-      if (k + 1 < KT) iter(k + 1, sA1, sW1, sA0, sW0);
+      __syncthreads();
+      step(sA0, sW0, k + 1, sA1, sW1, do_c);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      step(sA1, sW1, k + 2 < KT ? k + 2 : -1, sA0, sW0, do_c);
     }
-    if (gp == 0) ping_pong_barrier();
+    if (k < KT) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      step(sA0, sW0, -1, sA1, sW1, do_c);
+    }
   };
-  if (nbm == 2) run(std::integral_constant<int, 2>{});
-  else if (nbm == 1) run(std::integral_constant<int, 1>{});
-  else run(std::integral_constant<int, 0>{});
+  if (wave_row0 < M) run(std::true_type{});
+  else run(std::false_type{});
 
-  store_tile<EPI, BNT>(acc, C, R, M, N, tm, tn, wm, wn, lane);
+  store_rows<EPI, BNT, 4>(acc, C, R, M, N, wave_row0, tn, wn, lane);
 }
 
 }  // namespace
@@ -527,7 +567,7 @@ hipError_t launch_gemm_ex(const uint16_t* A, const uint16_t* W, const uint16_t* 
   const int n_tiles = tiles_m * tiles_n;
 #define BI_GEMM(E, T)                                                                                          \
   if (epi == E && bnt == T) {                                                                                  \
-    hipLaunchKernelGGL((gemm_pp_kernel<E, T>), dim3(n_tiles), dim3(NT), 0, s, A, W, R, C, int(M), int(N), int(K), \
+    hipLaunchKernelGGL((gemm_bf16_kernel<E, T>), dim3(n_tiles), dim3(NT4), 0, s, A, W, R, C, int(M), int(N), int(K), \
                        tiles_n, n_tiles);                                                                      \
     return hipGetLastError();                                                                                  \
   }
