@@ -20,38 +20,31 @@
 // the 256-wide int4 GEMM against the 192-wide bf16 GEMM on the same weight).
 //
 // Int4 weights ("Residual nondeterminism" in the M-0002 limitations warns of
-// de-quantisation kernels with atomic additions): each thread expands one
-// 32-element group -- code * fp16 scale, exact in fp32, one rounding to bf16
-// -- straight into the same LDS tile the bf16 path uses, so the int4 GEMM is
+// de-quantisation kernels with atomic additions): each thread expands the two
+// 32-element groups of one weight tile row per K step -- code * fp16 scale, exact
+// in fp32, one rounding to bf16 -- with plain stores into the same LDS tile layout
+// the bf16 path uses, so the int4 GEMM is
 // bit-identical to the bf16 GEMM on the de-quantised weight.  The expansion
 // takes ~2.4 VALU instructions per element (two codes per bit operation as fp16
 // pairs, one mixed-precision fma each, one packed bf16 conversion per pair).
 //
-// Int4 weights, register-staged schedule.  Data flow: global -> registers
-// (prefetch of step k+1 during step k) -> LDS
-// (two stages, 16-byte chunks xor-swizzled by row pair to keep ds_read_b128
-// and ds_write_b128 conflict-free) -> MFMA operands.  Step k+1's registers go
-// into the free LDS stage in the middle of step k's MFMA stream (after its
-// third substep), so the stores and their wait for the global loads overlap
-// the matrix work; one barrier per step.  Inside a step the fragments of k-substep
-// kk+1 are read while the MFMAs of kk run, one LDS read between consecutive
-// MFMAs (scheduling hints), and the MFMA phase runs at raised wave priority
-// so the SIMD's other wave issues its memory work in the gaps.  MFMA operand
-// A is the weight tile, operand B the activation tile, so each lane ends with
-// 4 consecutive output columns of one output row and stores them as one
-// 8-byte write.
-//
-// bf16 weights use a second schedule with the same per-element MFMA chain (so
-// the same bits): four waves, one per SIMD, each owning a 128 x BNT/2 block of
-// the tile (256 accumulator registers): 0.5 LDS fragment reads per MFMA against
-// 0.75 for eight 64-row waves.  Both operand tiles go from global memory
-// straight into LDS (global_load_lds_dwordx4, no staging registers), a stage
-// ahead, each LDS stage a separate array so the compiler can tell the pending
-// loads from the reads.  The wave issues, between the MFMAs of each 16-deep
-// substep, the next substep's fragment reads and the next stage's direct loads
-// in a fixed interleaved order: issued in one burst, the loads held up the
-// in-order MFMA stream behind them.  Operand offsets are 32-bit and relative to
-// the tile's first rows, so one schedule serves every operand size.
+// Schedule (both kernels).  Four waves, one per SIMD, each owning a 128 x BNT/2
+// block of the tile (256 accumulator registers): 0.5 LDS fragment reads per MFMA
+// against 0.75 for eight 64-row waves.  Operand tiles sit in LDS in two stages
+// (16-byte chunks xor-swizzled by row pair, so ds_read_b128 is conflict-free),
+// each stage a separate array so the compiler can tell the loads in flight from
+// the reads; one barrier per 64-deep K step.  The activation tile (and the bf16
+// weight tile) goes from global memory straight into LDS (global_load_lds_dwordx4,
+// no staging registers), a stage ahead.  Int4 weights: each thread owns one weight
+// tile row, loads its codes and scales into registers two stages ahead and
+// de-quantises them into the free LDS stage one stage ahead.  The wave issues,
+// between the MFMAs of each 16-deep substep, the next substep's fragment reads and
+// the next stages' loads and de-quantisation in a fixed interleaved order: issued
+// in one burst, the loads held up the in-order MFMA stream behind them.  MFMA
+// operand A is the weight tile, operand B the activation tile, so each lane ends
+// with 4 consecutive output columns of one output row and stores them as one
+// 8-byte write.  Operand offsets are 32-bit and relative to the tile's first rows,
+// so one schedule serves every operand size.
 #include <type_traits>
 #include <utility>
 
@@ -62,10 +55,8 @@ namespace bi {
 namespace {
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int NT = 512;                 // int4: 8 waves, 2 along N (half the tile width each) x 4 along M (64 each)
-constexpr int NT4 = 256;                // bf16: 4 waves, 2 along N x 2 along M (128 each), one per SIMD
+constexpr int NT4 = 256;                // 4 waves, 2 along N x 2 along M (128 rows each), one per SIMD
 constexpr int TILE = BM * BK;           // bf16 elements of one operand tile (BM == BN)
-constexpr int kStoreAfter = 2;         // the next stage is written to LDS after this substep's MFMAs
 static_assert(BM == BN, "square tile assumed by the LDS layout");
 
 // Work-group -> tile.  Work-groups are dealt round-robin to the 8 XCDs (work-group
@@ -114,18 +105,6 @@ __device__ __forceinline__ uint4 dequant8(uint32_t word, float sc, float nb) {
     f[j + 4] = __builtin_fmaf(float(p[1]), sc, nb);
   }
   return make_uint4(pack2bf(f[0], f[1]), pack2bf(f[2], f[3]), pack2bf(f[4], f[5]), pack2bf(f[6], f[7]));
-}
-
-// Expand one int4 group (16 bytes = 32 codes, one fp16 scale) into four bf16 16-byte
-// chunks of tile row `row`.
-__device__ __forceinline__ void dequant_group_to_lds(const uint4& rq, uint16_t rs, uint16_t* sW,
-                                                     int row, int half) {
-  const float s = float(__builtin_bit_cast(_Float16, rs));
-  const float nb = -1032.0f * s;
-  const uint32_t words[4] = {rq.x, rq.y, rq.z, rq.w};
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    *reinterpret_cast<uint4*>(sW + lds_off(row, half * 4 + c)) = dequant8(words[c], s, nb);
 }
 
 // Epilogues.  kEpiPlain: C = bf16(acc).  kEpiResid: C = bf16(R + bf16(acc)), the residual
@@ -194,173 +173,6 @@ __device__ __forceinline__ void store_rows(const f32x16 (&acc)[BNT / 64][NBR], u
       }
     }
   }
-}
-
-// the int4 kernel's waves: two 32-row blocks at tile rows wm*64 ..
-template <int EPI, int BNT>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[BNT / 64][2], uint16_t* C,
-                                           const uint16_t* R, int M, int N, int tm, int tn,
-                                           int wm, int wn, int lane) {
-  store_rows<EPI, BNT, 2>(acc, C, R, M, N, tm * BM + wm * 64, tn, wn, lane);
-}
-
-// int4-weight GEMM, register-staged schedule (see the file comment), BM x BNT x BK tiles.
-template <int EPI, int BNT>
-__global__ __launch_bounds__(NT, 1) void gemm_w4_kernel(const uint16_t* __restrict__ A,
-                                                        const uint8_t* __restrict__ Wq,
-                                                        const uint16_t* __restrict__ Ws,
-                                                        const uint16_t* R,  // may alias C (resid)
-                                                        uint16_t* C, int M, int N, int K,
-                                                        int tiles_n, int n_tiles) {
-  static_assert(BNT == 256 || (BNT == 192 && EPI != kEpiGated), "tile width");
-  constexpr int NB = BNT / 64;  // 32-column blocks per wave (two waves along N)
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2][2][TILE];
-
-  const int tile = tile_of(blockIdx.x, n_tiles, tiles_n);
-  const int tm = tile / tiles_n;
-  const int tn = tile % tiles_n;
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wn = wave & 1;   // BNT / 2 output columns
-  const int wm = wave >> 1;  // 64 output rows
-
-  // ---- global load assignment
-  // A tile: 256 rows x 8 chunks; thread t loads chunk (t & 7) of rows (t >> 3) + 64 i.
-  // W tile: thread t expands the 32-code group t & 1 of tile row q_row.  A 192-wide tile
-  // uses rows 0 .. 191 of the LDS tile; the threads of rows 192 .. 255 expand a clamped row
-  // into the unused rest (no branch in the loop).
-  // Rows past M (past N for W) are clamped: computed, never stored.
-  const int ld_chunk = t & 7;
-  const int ld_row = t >> 3;
-  const int a_last = M - 1, w_last = (EPI == kEpiGated ? 2 * N : N) - 1;
-  const uint16_t* a_base = A + ld_chunk * 8;
-  int a_r0 = min(tm * BM + ld_row, a_last), a_r1 = min(tm * BM + ld_row + 64, a_last);
-  int a_r2 = min(tm * BM + ld_row + 128, a_last), a_r3 = min(tm * BM + ld_row + 192, a_last);
-  // Each 8-lane group of a wave writes 4 rows whose swizzle keys (row / 2) % 8 are
-  // 4 a + 0..3 (rows 8 a + p, + 2, + 4, + 6), both halves each: the 8 lanes' 16-byte chunks
-  // of one write instruction land on 8 distinct chunk positions (no bank conflict).
-  const int q_row = 8 * (t >> 4) + 2 * ((t >> 1) & 3) + ((t >> 3) & 1);
-  const int q_half = t & 1;
-  const int q_r = min(w_row<EPI, BNT>(tn, q_row, N), w_last);
-  const uint8_t* q_src = Wq + int64_t(q_r) * (K / 2) + q_half * 16;
-  const uint16_t* s_src = Ws + int64_t(q_r) * (K / 32) + q_half;
-
-  uint4 ra0, ra1, ra2, ra3, rq;
-  uint16_t rs = 0;
-
-#define BI_LOAD_GLOBAL(kt)                                                                  \
-  do {                                                                                      \
-    const int ko = (kt) * BK;                                                               \
-    ra0 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r0) * K + ko);                 \
-    ra1 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r1) * K + ko);                 \
-    ra2 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r2) * K + ko);                 \
-    ra3 = *reinterpret_cast<const uint4*>(a_base + int64_t(a_r3) * K + ko);                 \
-    rq = *reinterpret_cast<const uint4*>(q_src + (kt) * (BK / 2));                          \
-    rs = s_src[(kt) * (BK / 32)];                                                           \
-  } while (0)
-
-#define BI_STORE_LDS(stage)                                                                 \
-  do {                                                                                      \
-    uint16_t* sA = smem[stage][0];                                                          \
-    uint16_t* sW = smem[stage][1];                                                          \
-    *reinterpret_cast<uint4*>(sA + lds_off(ld_row, ld_chunk)) = ra0;                        \
-    *reinterpret_cast<uint4*>(sA + lds_off(ld_row + 64, ld_chunk)) = ra1;                   \
-    *reinterpret_cast<uint4*>(sA + lds_off(ld_row + 128, ld_chunk)) = ra2;                  \
-    *reinterpret_cast<uint4*>(sA + lds_off(ld_row + 192, ld_chunk)) = ra3;                  \
-    dequant_group_to_lds(rq, rs, sW, q_row, q_half);                                        \
-  } while (0)
-
-  f32x16 acc[NB][2];
-#pragma unroll
-  for (int bn = 0; bn < NB; ++bn)
-#pragma unroll
-    for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[bn][bm][r] = 0.f;
-
-  const int frag_row = lane & 31;
-  const int frag_chunk = lane >> 5;
-  // MFMA work of one stage for the wave's first NBM 32-row blocks.  Blocks
-  // that lie entirely past M are skipped: that removes only padding work and
-  // leaves every valid element's instruction sequence unchanged.  A wave with
-  // no block left still loads and stores its share of every tile and meets
-  // every barrier.  `store` (the next stage's LDS writes) runs after the MFMAs
-  // of substep SAT (-1: no store).
-  const int wave_row0 = tm * BM + wm * 64;
-  const int nbm = wave_row0 >= M ? 0 : (wave_row0 + 32 >= M ? 1 : 2);
-  auto compute_stage = [&](const uint16_t* sA, const uint16_t* sW, auto nbm_c, auto store_c, auto&& store) {
-    constexpr int NBM = decltype(nbm_c)::value;
-    constexpr int SAT = decltype(store_c)::value;
-    if constexpr (NBM == 0) {
-      if constexpr (SAT >= 0) store();
-    } else {
-      bf16x8 wf[2][NB], af[2][NBM];
-#pragma unroll
-      for (int bm = 0; bm < NBM; ++bm)
-        af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * 64 + bm * 32 + frag_row, frag_chunk));
-#pragma unroll
-      for (int bn = 0; bn < NB; ++bn)
-        wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + lds_off(wn * (BNT / 2) + bn * 32 + frag_row, frag_chunk));
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        const int cb = kk & 1, nb = cb ^ 1;
-        if (kk + 1 < BK / 16) {
-          // read in the order the next substep uses them: A fragments, then W
-#pragma unroll
-          for (int bm = 0; bm < NBM; ++bm)
-            af[nb][bm] = *reinterpret_cast<const bf16x8*>(
-                sA + lds_off(wm * 64 + bm * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
-#pragma unroll
-          for (int bn = 0; bn < NB; ++bn)
-            wf[nb][bn] = *reinterpret_cast<const bf16x8*>(
-                sW + lds_off(wn * (BNT / 2) + bn * 32 + frag_row, (kk + 1) * 2 + frag_chunk));
-        }
-#pragma unroll
-        for (int bn = 0; bn < NB; ++bn)
-#pragma unroll
-          for (int bm = 0; bm < NBM; ++bm)
-            acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][bn], af[cb][bm], acc[bn][bm], 0, 0, 0);
-        if (kk == SAT) store();
-        if (kk + 1 < BK / 16) {
-          // one fragment read between consecutive MFMAs
-#pragma unroll
-          for (int i = 0; i < NBM + NB; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          if constexpr (NB * NBM > NBM + NB) __builtin_amdgcn_sched_group_barrier(0x008, NB * NBM - NBM - NB, 0);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-  };
-
-  const int KT = K / BK;
-  BI_LOAD_GLOBAL(0);
-  BI_STORE_LDS(0);
-  __syncthreads();
-
-  auto run = [&](auto nbm_c) {
-    for (int kt = 0; kt + 1 < KT; ++kt) {
-      const int cur = kt & 1;
-      BI_LOAD_GLOBAL(kt + 1);
-      compute_stage(smem[cur][0], smem[cur][1], nbm_c, std::integral_constant<int, kStoreAfter>{},
-                    [&] { BI_STORE_LDS(cur ^ 1); });
-      __syncthreads();
-    }
-    const int cur = (KT - 1) & 1;
-    compute_stage(smem[cur][0], smem[cur][1], nbm_c, std::integral_constant<int, -1>{}, [] {});
-  };
-  if (nbm == 2) run(std::integral_constant<int, 2>{});
-  else if (nbm == 1) run(std::integral_constant<int, 1>{});
-  else run(std::integral_constant<int, 0>{});
-
-  store_tile<EPI, BNT>(acc, C, R, M, N, tm, tn, wm, wn, lane);
-#undef BI_LOAD_GLOBAL
-#undef BI_STORE_LDS
 }
 
 // s_waitcnt immediate (gfx9 layout: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -550,6 +362,179 @@ __global__ __launch_bounds__(NT4, 1) void gemm_bf16_kernel(const uint16_t* __res
   store_rows<EPI, BNT, 4>(acc, C, R, M, N, wave_row0, tn, wn, lane);
 }
 
+// int4-weight GEMM, four waves of 128 x BNT/2 like the bf16 kernel.  A goes global -> LDS
+// directly; each thread owns one W tile row: its 64 codes and two group scales of stage
+// k + 2 are loaded into registers during step k (substep 1), and those of stage k + 1
+// (loaded during step k - 1) are de-quantised into the free LDS stage during substeps 2
+// and 3, interleaved with the MFMAs.
+template <int EPI, int BNT>
+__global__ __launch_bounds__(NT4, 1) void gemm_w4_kernel(const uint16_t* __restrict__ A,
+                                                          const uint8_t* __restrict__ Wq,
+                                                          const uint16_t* __restrict__ Ws,
+                                                          const uint16_t* R,  // may alias C (resid)
+                                                          uint16_t* C, int M, int N, int K,
+                                                          int tiles_n, int n_tiles) {
+  static_assert(BNT == 256 || (BNT == 192 && EPI != kEpiGated), "tile width");
+  constexpr int NB = BNT / 64;
+  constexpr int NM = NB * 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t sW1[TILE];
+
+  const int tile = tile_of(blockIdx.x, n_tiles, tiles_n);
+  const int tm = tile / tiles_n;
+  const int tn = tile % tiles_n;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = int(__builtin_amdgcn_readfirstlane(t >> 6));
+  const int wn = wave & 1;
+  const int wm = wave >> 1;
+
+  const uint16_t* At = A + int64_t(tm) * BM * K;
+  const int a_rows = min(BM, M - tm * BM);
+  uint32_t a_vo[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 64 * wave + 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    a_vo[j] = uint32_t(min(row, a_rows - 1)) * uint32_t(K) * 2u + uint32_t(chunk) * 16u;
+  }
+  auto load_a = [&](int kt, uint16_t* dA, int j) {
+    load_lds_b128(reinterpret_cast<const char*>(At + kt * BK) + a_vo[j], dA + (8 * wave + j) * 512);
+  };
+  // W tile row of thread t: each 8-lane group takes rows 16 a + p + 0, 2, .., 14, whose
+  // swizzle keys (row / 2) % 8 are 0 .. 7, so the group's 16-byte writes of one chunk index
+  // land on 8 distinct chunk positions.  A 192-wide tile uses rows 0 .. 191; the threads of
+  // rows 192 .. 255 expand a clamped row into the unused rest.
+  const int q_row = 16 * (t >> 4) + 2 * (t & 7) + ((t >> 3) & 1);
+  const int w_last = (EPI == kEpiGated ? 2 * N : N) - 1;
+  const int q_r = min(w_row<EPI, BNT>(tn, q_row, N), w_last);
+  const uint8_t* q_src = Wq + int64_t(q_r) * (K / 2);
+  const uint16_t* s_src = Ws + int64_t(q_r) * (K / 32);
+  uint4 wc[2][2];      // [register set][half]: 64 codes of one stage
+  uint32_t wsc[2];     // [register set]: the two group scales (fp16 pair)
+  auto load_w = [&](int kt, int set, int x) {
+    if (x < 2) wc[set][x] = *reinterpret_cast<const uint4*>(q_src + int64_t(kt) * (BK / 2) + 16 * x);
+    else wsc[set] = *reinterpret_cast<const uint32_t*>(s_src + int64_t(kt) * (BK / 32));
+  };
+  auto dequant_w = [&](int set, uint16_t* dW, int j) {  // chunk j (codes 8 j .. 8 j + 7)
+    const uint32_t sc2 = wsc[set];
+    const float s = float(__builtin_bit_cast(_Float16, uint16_t(j < 4 ? sc2 & 0xFFFFu : sc2 >> 16)));
+    const uint4 h = wc[set][j >> 2];
+    const uint32_t w = (j & 3) == 0 ? h.x : (j & 3) == 1 ? h.y : (j & 3) == 2 ? h.z : h.w;
+    *reinterpret_cast<uint4*>(dW + lds_off(q_row, j)) = dequant8(w, s, -1032.0f * s);
+  };
+
+  f32x16 acc[NB][4];
+#pragma unroll
+  for (int bn = 0; bn < NB; ++bn)
+#pragma unroll
+    for (int bm = 0; bm < 4; ++bm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[bn][bm][r] = 0.f;
+
+  const int fr = lane & 31, fc = lane >> 5;
+  const int fkey = (fr >> 1) & 7;
+  const int a_base = (wm * 128) * BK, w_base = (wn * (BNT / 2)) * BK;
+  const int wave_row0 = tm * BM + wm * 128;
+
+  // one K step from stage (sA, sW); ka: stage whose A loads and W de-quantisation (from
+  // register set DQ into nW) go into (nA, nW), kw: stage whose W codes are loaded into
+  // register set 1 - DQ (-1: none)
+  auto step = [&](const uint16_t* sA, const uint16_t* sW, int ka, int kw, uint16_t* nA, uint16_t* nW,
+                  auto dq_c, auto do_c) {
+    constexpr int DQ = decltype(dq_c)::value;
+    if constexpr (!decltype(do_c)::value) {
+      if (ka >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) load_a(ka, nA, j);
+      }
+      if (kw >= 0) {
+#pragma unroll
+        for (int x = 0; x < 3; ++x) load_w(kw, 1 - DQ, x);
+      }
+      if (ka >= 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dequant_w(DQ, nW, j);
+      }
+    } else {
+      bf16x8 wf[2][NB], af[2][4];
+      {
+        const int lo = fr * BK + ((fc ^ fkey) << 3);
+#pragma unroll
+        for (int bm = 0; bm < 4; ++bm) af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo + bm * 32 * BK);
+#pragma unroll
+        for (int bn = 0; bn < NB; ++bn) wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo + bn * 32 * BK);
+      }
+      static_for<BK / 16>([&](auto kk_c) {
+        constexpr int kk = decltype(kk_c)::value;
+        constexpr int cb = kk & 1;
+        constexpr int nr = kk + 1 < BK / 16 ? 4 + NB : 0;
+        constexpr int nd = kk == 0 ? 8 : (kk == 1 ? 3 : 4);
+        const int lo_n = fr * BK + (((2 * (kk + 1) + fc) ^ fkey) << 3);
+        static_for<NM>([&](auto i_c) {
+          constexpr int i = decltype(i_c)::value;
+          acc[i >> 2][i & 3] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][i >> 2], af[cb][i & 3], acc[i >> 2][i & 3], 0, 0, 0);
+          constexpr int q0 = issue_first(i, nr + nd, NM);
+          static_for<issue_first(i + 1, nr + nd, NM) - q0>([&](auto d_c) {
+            constexpr int q = q0 + decltype(d_c)::value;
+            constexpr int x = issue_index(q, nr, nd);
+            if constexpr (issue_kind(q, nr, nd) == 0) {
+              if constexpr (x < 4) af[cb ^ 1][x] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo_n + x * 32 * BK);
+              else wf[cb ^ 1][x - 4] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo_n + (x - 4) * 32 * BK);
+            } else if constexpr (kk == 0) {
+              if (ka >= 0) load_a(ka, nA, x);
+            } else if constexpr (kk == 1) {
+              if (kw >= 0) load_w(kw, 1 - DQ, x);
+            } else {
+              if (ka >= 0) dequant_w(DQ, nW, 4 * (kk - 2) + x);
+            }
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      });
+    }
+  };
+
+  // prologue: stage 0 (A direct, W codes of stages 0 and 1 into register sets 0 and 1,
+  // stage 0 de-quantised into sW0)
+  const int KT = K / BK;
+  auto run = [&](auto do_c) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) load_a(0, sA0, j);
+#pragma unroll
+    for (int x = 0; x < 3; ++x) load_w(0, 0, x);
+    if (KT > 1) {
+#pragma unroll
+      for (int x = 0; x < 3; ++x) load_w(1, 1, x);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dequant_w(0, sW0, j);
+    int k = 0;
+    for (; k + 1 < KT; k += 2) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      step(sA0, sW0, k + 1, k + 2 < KT ? k + 2 : -1, sA1, sW1, std::integral_constant<int, 1>{}, do_c);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      step(sA1, sW1, k + 2 < KT ? k + 2 : -1, k + 3 < KT ? k + 3 : -1, sA0, sW0, std::integral_constant<int, 0>{},
+           do_c);
+    }
+    if (k < KT) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      step(sA0, sW0, -1, -1, sA1, sW1, std::integral_constant<int, 1>{}, do_c);
+    }
+  };
+  if (wave_row0 < M) run(std::true_type{});
+  else run(std::false_type{});
+
+  store_rows<EPI, BNT, 4>(acc, C, R, M, N, wave_row0, tn, wn, lane);
+}
+
 }  // namespace
 
 // Column-tile width of the bf16 GEMM for a weight of N rows: 256, or 192 for weights of at
@@ -585,7 +570,7 @@ hipError_t launch_gemm_w4_ex(const uint8_t* Wq, const uint16_t* Ws, const uint16
   const int n_tiles = tiles_m * tiles_n;
 #define BI_GEMM(E, T)                                                                                          \
   if (epi == E && bnt == T) {                                                                                  \
-    hipLaunchKernelGGL((gemm_w4_kernel<E, T>), dim3(n_tiles), dim3(NT), 0, s, A, Wq, Ws, R, C, int(M), int(N),   \
+    hipLaunchKernelGGL((gemm_w4_kernel<E, T>), dim3(n_tiles), dim3(NT4), 0, s, A, Wq, Ws, R, C, int(M), int(N),  \
                        int(K), tiles_n, n_tiles);                                                              \
     return hipGetLastError();                                                                                  \
   }
