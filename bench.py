@@ -42,17 +42,23 @@ def parse():
     p.add_argument("--batch", type=int, default=256, help="decode requests in the mixed step")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-reps", type=int, default=10)
+    p.add_argument("--warm-ms", type=float, default=30.0,
+                   help="warm-up before each standalone kernel timing (0: none, a fixed launch count for profiling)")
     p.add_argument("--decode-order", default="split", choices=["split", "prefill"],
                    help="decode attention: fixed 256-key split (default) or the prefill kernel's key order")
     return p.parse_args()
 
 
 # --------------------------------------------------------------- helpers
-def event_time_ms(torch, fn, reps, warm_ms=30.0, groups=3):
+WARM_MS = 30.0
+
+
+def event_time_ms(torch, fn, reps, warm_ms=None, groups=3):
     """Average duration of fn() (kernels on torch's current stream) with HIP events: after
     at least warm_ms of back-to-back warm-up calls (the clock needs a few milliseconds of
     load to reach its working frequency after the host has left the GPU idle), `groups`
     groups of `reps` back-to-back calls are timed; the median group's average is returned."""
+    warm_ms = WARM_MS if warm_ms is None else warm_ms
     s = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -61,7 +67,7 @@ def event_time_ms(torch, fn, reps, warm_ms=30.0, groups=3):
     end.record(s)
     end.synchronize()
     first = max(start.elapsed_time(end), 1e-3)
-    for _ in range(min(2000, int(math.ceil(warm_ms / first)))):
+    for _ in range(min(2000, int(math.ceil(warm_ms / first))) if warm_ms > 0 else 0):
         fn()
     avg = []
     for _ in range(groups):
@@ -536,7 +542,9 @@ def run_copy(args, torch, bi, synth):
 
 
 def main():
+    global WARM_MS
     args = parse()
+    WARM_MS = args.warm_ms
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
