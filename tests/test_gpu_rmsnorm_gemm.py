@@ -140,7 +140,7 @@ def test_gemm_config2_invariance_and_parity():
 
 
 # ------------------------------------------------------------------ int4 GEMM
-@pytest.mark.parametrize("m,n,k", [(300, 264, 256), (70, 4096, 4096), (513, 512, 12288)])
+@pytest.mark.parametrize("m,n,k", [(300, 264, 256), (70, 4096, 4096), (513, 512, 12288), (40, 4104, 256)])
 def test_gemm_w4_equals_bf16_on_dequantised(m, n, k):
     device()
     announce("gemm_w4 vs bf16", m, n, k)
