@@ -362,15 +362,18 @@ def run_decode(args, torch, bi, synth):
 
 def run_norm(args, torch, bi, synth):
     """RMSNorm at 65536 x 4096 (the value), and at the blocks' own shapes: the int4 mixed
-    step (2304 x 4096) and the dense block's 4000-token prefill (4000 x 2560)."""
+    step (2304 x 4096) and the dense block's 4000-token prefill (4000 x 2560); torch's copy
+    of the same tensor (the same bytes read and written) timed beside each shape."""
     res = {}
     for M, H in ((65536, 4096), (2304, 4096), (4000, 2560)):
         x = synth.normal_bf16_device(1200 + H, (M, H))
         g = bi.to_dev(synth.normal_bf16(1201, (H,), 0.02, 1.0))
         y = torch.empty_like(x)
         t = event_time_ms(torch, lambda: bi.rmsnorm(x, g, 1e-6, out=y), max(args.kernel_reps, 20))
+        tc = event_time_ms(torch, lambda: y.copy_(x), max(args.kernel_reps, 20))  # same bytes, torch's copy
         by = 2.0 * M * H * 2
-        res[f"{M}x{H}"] = {"ms": t, "gbs": by / t / 1e6, "frac": by / t / 1e6 / (PEAK_HBM / 1e9)}
+        res[f"{M}x{H}"] = {"ms": t, "gbs": by / t / 1e6, "frac": by / t / 1e6 / (PEAK_HBM / 1e9),
+                           "torch_copy_same_bytes_gbs": by / tc / 1e6}
         del x, y
     big = res["65536x4096"]
     return {"metric": "RMSNorm GB/s", "value": big["gbs"], "unit": "GB/s", "ms": big["ms"], "frac": big["frac"],
