@@ -100,13 +100,25 @@ def rowwise_norm_report(gpu_bits, ref_bits, rel: float = REL_TOL):
     den = np.linalg.norm(r, axis=1)
     ratio = num / np.maximum(den, 1e-30)
     elem = tolerance_report(gpu_bits, ref_bits, rel)
+    # per element, the absolute term at the row's scale: |g - r| <= rel |r| + 2 rel rms(r_row).
+    # End to end an element's error is dominated by a noise floor proportional to its row's
+    # RMS (one-ulp disagreements of intermediate roundings spread by the next contraction);
+    # measured on the hidden-2560 block its standard deviation is ~0.26 % of the RMS, so
+    # 2 rel = 1.6 % is ~6 standard deviations over 1.5 M elements.
+    rms = den / np.sqrt(r.shape[1])
+    excess = np.abs(g.astype(np.float64) - r) / np.maximum(rel * np.abs(r) + 2 * rel * rms[:, None], 1e-300)
     return {"rows": len(g), "bad_rows": int((ratio > rel).sum()), "max_row_rel": float(ratio.max()),
             "mean_row_rel": float(ratio.mean()), "elementwise_violations": elem["violations"],
-            "elements": elem["n"], "bitwise_equal": elem["bitwise_equal"]}
+            "elements": elem["n"], "bitwise_equal": elem["bitwise_equal"],
+            "row_scaled_violations": int((excess > 1.0).sum()), "max_row_scaled_ratio": float(excess.max())}
 
 
 def assert_rowwise_norm(gpu_bits, ref_bits, what: str = ""):
+    """Both end-to-end rules: every row within rel in norm, and every element within
+    rel |ref| + 2 rel rms(its row) (the per-element rule with its absolute term taken at the
+    row's own scale, where the stage-wise rule uses 1e-3)."""
     rep = rowwise_norm_report(gpu_bits, ref_bits)
     print(f"{what} end-to-end: {rep}")
     assert rep["bad_rows"] == 0, f"{what}: {rep}"
+    assert rep["row_scaled_violations"] == 0, f"{what}: {rep}"
     return rep
