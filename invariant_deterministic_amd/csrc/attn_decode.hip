@@ -346,20 +346,23 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(
 }
 
 // Exclusive prefix sum over a 1024-thread work-group; `total` receives the sum.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* s_w, int& total) {
+// Exclusive prefix sum over a 1024-thread work-group (16 waves) of a 64-bit value; the
+// work-group's total in `total`.  Packed fields add independently as long as no field's
+// total overflows.
+__device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t v, uint64_t* s_w, uint64_t& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int x = v;
+  uint64_t x = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, 64);
+    const uint64_t y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
   if (lane == 63) s_w[w] = x;
   __syncthreads();
-  int before = 0, all = 0;
+  uint64_t before = 0, all = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int t = s_w[i];
+    const uint64_t t = s_w[i];
     before += i < w ? t : 0;
     all += t;
   }
@@ -372,46 +375,48 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_w, int& total)
 // arrays into DecodeSeq and lists the runs (request, first unit) with the most units first
 // (every full run in request order, then the last runs of 7, 6, .., 1 units, each in
 // request order; the order the block entry point's host list has).  A request whose length
-// is outside 1 .. max_len gets no run (the combine kernel writes NaN for it).
+// is outside 1 .. max_len gets no run (the combine kernel writes NaN for it).  Counts of the
+// seven partial-run classes travel packed in 16-bit fields of two 64-bit words (classes
+// 1..4 and 5..7; no class holds more than B <= 65535 runs), full runs in a third word, so
+// each pass takes three work-group scans; every thread keeps the class bases itself.
 __global__ __launch_bounds__(1024) void decode_prep_kernel(const int64_t* __restrict__ kv_offset,
                                                            const int32_t* __restrict__ kv_len, int B,
                                                            int64_t max_len, DecodeSeq* __restrict__ seqs,
                                                            int2* __restrict__ runs, int* __restrict__ n_runs) {
   constexpr int R = kDecodeRun;
-  __shared__ int s_w[16];
-  __shared__ int s_base[R + 1];  // next free position of each class: R full runs, k < R last runs of k units
+  static_assert(R == 8, "seven partial-run classes, packed four and three per word");
+  __shared__ uint64_t s_w[16];
   auto units = [&](int b) -> int {
     const int64_t L = kv_len[b];
     return (L >= 1 && L <= max_len) ? int((L + kSplit - 1) / kSplit) : 0;
   };
-  // pass 1: runs per class; a thread's counts packed in 8-bit fields (classes 1 .. R - 1,
-  // at most 64 requests each per thread while B <= 65536) and one count of full runs
-  static_assert(R == 8, "class counts are packed for runs of 8 units");
-  uint64_t packed = 0;
-  int full = 0;
+  auto field = [](int p) -> uint64_t { return uint64_t(1) << (16 * ((p - 1) & 3)); };
+  auto count = [](uint64_t lo, uint64_t hi, int k) -> int {  // class k = 1 .. 7
+    return int(((k <= 4 ? lo : hi) >> (16 * ((k - 1) & 3))) & 0xFFFF);
+  };
+  // pass 1: runs per class
+  uint64_t lo = 0, hi = 0, full = 0;
   for (int b = threadIdx.x; b < B; b += 1024) {
     const int U = units(b);
-    full += U / R;
-    if (U % R) packed += uint64_t(1) << (8 * (U % R));
+    full += uint64_t(U / R);
+    const int p = U % R;
+    if (p) (p <= 4 ? lo : hi) += field(p);
   }
-  for (int k = R; k >= 1; --k) {
-    const int c = k == R ? full : int((packed >> (8 * k)) & 0xFF);
-    int tot;
-    block_exclusive_scan(c, s_w, tot);
-    if (threadIdx.x == 0) s_base[k] = tot;  // the class's count, turned into its base below
+  uint64_t t_lo, t_hi, t_full;
+  block_exclusive_scan(lo, s_w, t_lo);
+  block_exclusive_scan(hi, s_w, t_hi);
+  block_exclusive_scan(full, s_w, t_full);
+  // bases: full runs first, then the classes 7, 6, .., 1
+  int base[R + 1];
+  base[R] = 0;
+  int at = int(t_full);
+#pragma unroll
+  for (int k = R - 1; k >= 1; --k) {
+    base[k] = at;
+    at += count(t_lo, t_hi, k);
   }
-  if (threadIdx.x == 0) {
-    int at = 0;
-    for (int k = R; k >= 1; --k) {
-      const int n = s_base[k];
-      s_base[k] = at;
-      at += n;
-    }
-    *n_runs = at;
-  }
-  __syncthreads();
-  // pass 2: positions, 1024 requests at a time in request order.  s_base[k] is read before
-  // the class's scan and advanced by thread 0 after it (the scan's barriers order the two).
+  if (threadIdx.x == 0) *n_runs = at;
+  // pass 2: positions, 1024 requests at a time in request order
   for (int c = 0; c < B; c += 1024) {
     const int b = c + int(threadIdx.x);
     int U = 0;
@@ -425,18 +430,18 @@ __global__ __launch_bounds__(1024) void decode_prep_kernel(const int64_t* __rest
       U = units(b);
     }
     const int f = U / R, p = U % R;
-    for (int k = R; k >= 1; --k) {
-      const int v = k == R ? f : int(p == k);
-      const int bk = s_base[k];
-      int tot;
-      const int at = block_exclusive_scan(v, s_w, tot);
-      if (k == R) {
-        for (int i = 0; i < f; ++i) runs[bk + at + i] = make_int2(b, i * R);
-      } else if (v) {
-        runs[bk + at] = make_int2(b, f * R);
-      }
-      if (threadIdx.x == 0) s_base[k] = bk + tot;
-    }
+    uint64_t c_lo, c_hi, c_full;
+    const uint64_t x_lo = block_exclusive_scan(p >= 1 && p <= 4 ? field(p) : 0, s_w, c_lo);
+    const uint64_t x_hi = block_exclusive_scan(p >= 5 ? field(p) : 0, s_w, c_hi);
+    const uint64_t x_full = block_exclusive_scan(uint64_t(f), s_w, c_full);
+    for (int i = 0; i < f; ++i) runs[base[R] + int(x_full) + i] = make_int2(b, i * R);
+    int bp = 0;  // base of class p (a select chain: no runtime index into base[])
+#pragma unroll
+    for (int k = 1; k < R; ++k) bp = p == k ? base[k] : bp;
+    if (p) runs[bp + count(x_lo, x_hi, p)] = make_int2(b, f * R);
+    base[R] += int(c_full);
+#pragma unroll
+    for (int k = 1; k < R; ++k) base[k] += count(c_lo, c_hi, k);
   }
 }
 
