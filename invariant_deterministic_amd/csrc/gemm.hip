@@ -9,7 +9,8 @@
 //    most 4096 rows (the width is a function of the weight alone); there is no M-dependent
 //    dispatch, no split-K and no stream-K, and rows past M are handled by
 //    clamping their loads and masking their stores in the same instruction
-//    stream;
+//    stream (a wave whose 128 rows all lie past M skips its MFMAs: padding
+//    work only);
 //  * each C[i, j] is accumulated by one lane of one MFMA chain: K is walked in
 //    64-wide steps in ascending order, each step as four 16-deep
 //    v_mfma_f32_32x32x16_bf16 instructions in ascending order;
@@ -218,7 +219,6 @@ __global__ __launch_bounds__(NT4, 1) void gemm_bf16_kernel(const uint16_t* __res
   static_assert(BNT == 256 || (BNT == 192 && EPI != kEpiGated), "tile width");
   constexpr int NB = BNT / 64;   // 32-column blocks per wave (two waves along N)
   constexpr int WB = BNT / 32;   // 1 KB blocks of the W tile each wave loads
-  constexpr int NM = NB * 4;     // MFMAs per 16-deep substep
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sW0[BNT * BK];
@@ -278,13 +278,16 @@ __global__ __launch_bounds__(NT4, 1) void gemm_bf16_kernel(const uint16_t* __res
   const int a_base = (wm * 128) * BK, w_base = (wn * (BNT / 2)) * BK;
   const int wave_row0 = tm * BM + wm * 128;
 
-  // One K step from stage (sA, sW): four 16-deep substeps of NM MFMAs.  The fragments of
+  // One K step from stage (sA, sW): four 16-deep substeps of NB NBM MFMAs.  The fragments of
   // substep kk + 1 are read, and stage kn's direct loads issued (A during substep 0, W
   // during substep 1; kn < 0: none), between the MFMAs of substep kk in a fixed order, each
-  // MFMA and what follows it fenced from the scheduler.  A wave whose 128 rows all lie past
-  // M (DO = false) only issues its loads: that removes padding work alone.
-  auto step = [&](const uint16_t* sA, const uint16_t* sW, int kn, uint16_t* nA, uint16_t* nW, auto do_c) {
-    if constexpr (!decltype(do_c)::value) {
+  // MFMA and what follows it fenced from the scheduler.  A wave with at most 32 valid rows
+  // computes its first 32-row block only (NBM = 1), one whose 128 rows all lie past M only
+  // issues its loads (NBM = 0): that removes padding work alone.
+  auto step = [&](const uint16_t* sA, const uint16_t* sW, int kn, uint16_t* nA, uint16_t* nW, auto nbm_c) {
+    constexpr int NBM = decltype(nbm_c)::value;  // 32-row blocks computed (4, or 1 when <= 32 rows are valid)
+    constexpr int NMB = NB * NBM;                // MFMAs per substep
+    if constexpr (NBM == 0) {
       if (kn >= 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) load_a(kn, nA, j);
@@ -292,31 +295,31 @@ __global__ __launch_bounds__(NT4, 1) void gemm_bf16_kernel(const uint16_t* __res
         for (int j = 0; j < WB; ++j) load_w(kn, nW, j);
       }
     } else {
-      bf16x8 wf[2][NB], af[2][4];
+      bf16x8 wf[2][NB], af[2][NBM];
       {
         const int lo = fr * BK + ((fc ^ fkey) << 3);
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm) af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo + bm * 32 * BK);
+        for (int bm = 0; bm < NBM; ++bm) af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo + bm * 32 * BK);
 #pragma unroll
         for (int bn = 0; bn < NB; ++bn) wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo + bn * 32 * BK);
       }
       static_for<BK / 16>([&](auto kk_c) {
         constexpr int kk = decltype(kk_c)::value;
         constexpr int cb = kk & 1;
-        constexpr int nr = kk + 1 < BK / 16 ? 4 + NB : 0;
+        constexpr int nr = kk + 1 < BK / 16 ? NBM + NB : 0;
         constexpr int nd = kk == 0 ? 8 : (kk == 1 ? WB : 0);
         const int lo_n = fr * BK + (((2 * (kk + 1) + fc) ^ fkey) << 3);
-        static_for<NM>([&](auto i_c) {
+        static_for<NMB>([&](auto i_c) {
           constexpr int i = decltype(i_c)::value;
-          acc[i >> 2][i & 3] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][i >> 2], af[cb][i & 3], acc[i >> 2][i & 3], 0, 0, 0);
-          constexpr int q0 = issue_first(i, nr + nd, NM);
-          static_for<issue_first(i + 1, nr + nd, NM) - q0>([&](auto d_c) {
+          constexpr int bn = i / NBM, bm = i % NBM;
+          acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][bn], af[cb][bm], acc[bn][bm], 0, 0, 0);
+          constexpr int q0 = issue_first(i, nr + nd, NMB);
+          static_for<issue_first(i + 1, nr + nd, NMB) - q0>([&](auto d_c) {
             constexpr int q = q0 + decltype(d_c)::value;
             constexpr int x = issue_index(q, nr, nd);
             if constexpr (issue_kind(q, nr, nd) == 0) {
-              if constexpr (x < 4) af[cb ^ 1][x] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo_n + x * 32 * BK);
-              else wf[cb ^ 1][x - 4] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo_n + (x - 4) * 32 * BK);
+              if constexpr (x < NBM) af[cb ^ 1][x] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo_n + x * 32 * BK);
+              else wf[cb ^ 1][x - NBM] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo_n + (x - NBM) * 32 * BK);
             } else {
               if (kn >= 0) {
                 if constexpr (kk == 0) load_a(kn, nA, x);
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(NT4, 1) void gemm_bf16_kernel(const uint16_t* __res
   // two steps at a time, so the buffers stay compile-time distinct (the compiler can then
   // tell the loads in flight from the reads); an odd last step follows it.
   const int KT = K / BK;
-  auto run = [&](auto do_c) {
+  auto run = [&](auto nbm_c) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) load_a(0, sA0, j);
 #pragma unroll
@@ -345,19 +348,20 @@ __global__ __launch_bounds__(NT4, 1) void gemm_bf16_kernel(const uint16_t* __res
     for (; k + 1 < KT; k += 2) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      step(sA0, sW0, k + 1, sA1, sW1, do_c);
+      step(sA0, sW0, k + 1, sA1, sW1, nbm_c);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      step(sA1, sW1, k + 2 < KT ? k + 2 : -1, sA0, sW0, do_c);
+      step(sA1, sW1, k + 2 < KT ? k + 2 : -1, sA0, sW0, nbm_c);
     }
     if (k < KT) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      step(sA0, sW0, -1, sA1, sW1, do_c);
+      step(sA0, sW0, -1, sA1, sW1, nbm_c);
     }
   };
-  if (wave_row0 < M) run(std::true_type{});
-  else run(std::false_type{});
+  if (wave_row0 + 32 < M) run(std::integral_constant<int, 4>{});
+  else if (wave_row0 < M) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
 
   store_rows<EPI, BNT, 4>(acc, C, R, M, N, wave_row0, tn, wn, lane);
 }
@@ -376,7 +380,6 @@ __global__ __launch_bounds__(NT4, 1) void gemm_w4_kernel(const uint16_t* __restr
                                                           int tiles_n, int n_tiles) {
   static_assert(BNT == 256 || (BNT == 192 && EPI != kEpiGated), "tile width");
   constexpr int NB = BNT / 64;
-  constexpr int NM = NB * 4;
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t sW0[TILE];
@@ -443,9 +446,11 @@ __global__ __launch_bounds__(NT4, 1) void gemm_w4_kernel(const uint16_t* __restr
   // register set DQ into nW) go into (nA, nW), kw: stage whose W codes are loaded into
   // register set 1 - DQ (-1: none)
   auto step = [&](const uint16_t* sA, const uint16_t* sW, int ka, int kw, uint16_t* nA, uint16_t* nW,
-                  auto dq_c, auto do_c) {
+                  auto dq_c, auto nbm_c) {
     constexpr int DQ = decltype(dq_c)::value;
-    if constexpr (!decltype(do_c)::value) {
+    constexpr int NBM = decltype(nbm_c)::value;  // 32-row blocks computed (4, or 1 when <= 32 rows are valid)
+    constexpr int NMB = NB * NBM;                // MFMAs per substep
+    if constexpr (NBM == 0) {
       if (ka >= 0) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) load_a(ka, nA, j);
@@ -459,31 +464,31 @@ __global__ __launch_bounds__(NT4, 1) void gemm_w4_kernel(const uint16_t* __restr
         for (int j = 0; j < 8; ++j) dequant_w(DQ, nW, j);
       }
     } else {
-      bf16x8 wf[2][NB], af[2][4];
+      bf16x8 wf[2][NB], af[2][NBM];
       {
         const int lo = fr * BK + ((fc ^ fkey) << 3);
 #pragma unroll
-        for (int bm = 0; bm < 4; ++bm) af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo + bm * 32 * BK);
+        for (int bm = 0; bm < NBM; ++bm) af[0][bm] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo + bm * 32 * BK);
 #pragma unroll
         for (int bn = 0; bn < NB; ++bn) wf[0][bn] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo + bn * 32 * BK);
       }
       static_for<BK / 16>([&](auto kk_c) {
         constexpr int kk = decltype(kk_c)::value;
         constexpr int cb = kk & 1;
-        constexpr int nr = kk + 1 < BK / 16 ? 4 + NB : 0;
+        constexpr int nr = kk + 1 < BK / 16 ? NBM + NB : 0;
         constexpr int nd = kk == 0 ? 8 : (kk == 1 ? 3 : 4);
         const int lo_n = fr * BK + (((2 * (kk + 1) + fc) ^ fkey) << 3);
-        static_for<NM>([&](auto i_c) {
+        static_for<NMB>([&](auto i_c) {
           constexpr int i = decltype(i_c)::value;
-          acc[i >> 2][i & 3] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][i >> 2], af[cb][i & 3], acc[i >> 2][i & 3], 0, 0, 0);
-          constexpr int q0 = issue_first(i, nr + nd, NM);
-          static_for<issue_first(i + 1, nr + nd, NM) - q0>([&](auto d_c) {
+          constexpr int bn = i / NBM, bm = i % NBM;
+          acc[bn][bm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cb][bn], af[cb][bm], acc[bn][bm], 0, 0, 0);
+          constexpr int q0 = issue_first(i, nr + nd, NMB);
+          static_for<issue_first(i + 1, nr + nd, NMB) - q0>([&](auto d_c) {
             constexpr int q = q0 + decltype(d_c)::value;
             constexpr int x = issue_index(q, nr, nd);
             if constexpr (issue_kind(q, nr, nd) == 0) {
-              if constexpr (x < 4) af[cb ^ 1][x] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo_n + x * 32 * BK);
-              else wf[cb ^ 1][x - 4] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo_n + (x - 4) * 32 * BK);
+              if constexpr (x < NBM) af[cb ^ 1][x] = *reinterpret_cast<const bf16x8*>(sA + a_base + lo_n + x * 32 * BK);
+              else wf[cb ^ 1][x - NBM] = *reinterpret_cast<const bf16x8*>(sW + w_base + lo_n + (x - NBM) * 32 * BK);
             } else if constexpr (kk == 0) {
               if (ka >= 0) load_a(ka, nA, x);
             } else if constexpr (kk == 1) {
@@ -501,7 +506,7 @@ __global__ __launch_bounds__(NT4, 1) void gemm_w4_kernel(const uint16_t* __restr
   // prologue: stage 0 (A direct, W codes of stages 0 and 1 into register sets 0 and 1,
   // stage 0 de-quantised into sW0)
   const int KT = K / BK;
-  auto run = [&](auto do_c) {
+  auto run = [&](auto nbm_c) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) load_a(0, sA0, j);
 #pragma unroll
@@ -517,20 +522,21 @@ __global__ __launch_bounds__(NT4, 1) void gemm_w4_kernel(const uint16_t* __restr
     for (; k + 1 < KT; k += 2) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      step(sA0, sW0, k + 1, k + 2 < KT ? k + 2 : -1, sA1, sW1, std::integral_constant<int, 1>{}, do_c);
+      step(sA0, sW0, k + 1, k + 2 < KT ? k + 2 : -1, sA1, sW1, std::integral_constant<int, 1>{}, nbm_c);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       step(sA1, sW1, k + 2 < KT ? k + 2 : -1, k + 3 < KT ? k + 3 : -1, sA0, sW0, std::integral_constant<int, 0>{},
-           do_c);
+           nbm_c);
     }
     if (k < KT) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      step(sA0, sW0, -1, -1, sA1, sW1, std::integral_constant<int, 1>{}, do_c);
+      step(sA0, sW0, -1, -1, sA1, sW1, std::integral_constant<int, 1>{}, nbm_c);
     }
   };
-  if (wave_row0 < M) run(std::true_type{});
-  else run(std::false_type{});
+  if (wave_row0 + 32 < M) run(std::integral_constant<int, 4>{});
+  else if (wave_row0 < M) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
 
   store_rows<EPI, BNT, 4>(acc, C, R, M, N, wave_row0, tn, wn, lane);
 }
