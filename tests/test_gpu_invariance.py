@@ -5,7 +5,7 @@ count the distinct answers; M-0002 `technical`: a fixed reduction order per
 element whatever the batch size).  Each report prints the rows compared, the
 percentage identical and the largest number of distinct outputs of a request.
 
-- bf16 GEMM, K = N = 4096: row i of C at M in {1, 7, 64, 513, 4096}, identity,
+- bf16 GEMM, K = N = 4096: row i of C at M in {1, 7, 64, 288, 385, 513, 4096}, identity,
   reversed and random orders (64 rows also alone, 10 times for 8 of them).
 - RMSNorm at hidden 2560 and 4096: rows alone and in batches up to 4096.
 - Decode attention, 32 / 8 heads x 128, KV lengths ~ U{1..32768}: 64 requests alone
@@ -38,7 +38,7 @@ def test_gemm_rows_invariance():
     every = tuple(range(4096))
     calls = [harness.Call(every, None, "M=4096 identity"), harness.Call(every[::-1], None, "M=4096 reversed"),
              harness.Call(tuple(int(i) for i in rng.permutation(4096)), None, "M=4096 random")]
-    for M in (1, 7, 64, 513):
+    for M in (1, 7, 64, 288, 385, 513):
         for name in ("random", "random again"):
             calls.append(harness.Call(tuple(int(i) for i in rng.choice(4096, M, replace=False)), None, f"M={M} {name}"))
     sample = [int(i) for i in rng.choice(4096, 64, replace=False)]

@@ -176,7 +176,9 @@ def test_gemm_w4_batch_invariance():
     wqd, wsd = torch.from_numpy(wq).cuda(), torch.from_numpy(ws.view(np.int16)).cuda()
     ref = bits(bi.gemm_w4(dev(A), wqd, wsd))
     rng = np.random.default_rng(3202)
-    for M in (1, 2, 65, 2049, 2304):
+    # 288 / 289 / 385: a last tile row whose first 128-row wave has 32 / 33 valid rows, and one
+    # whose second wave has a single valid row (the one-block and four-block paths side by side)
+    for M in (1, 2, 65, 288, 289, 385, 2049, 2304):
         announce("gemm_w4 invariance", M)
         idx = rng.choice(2304, size=M, replace=False)
         assert_bitwise(bits(bi.gemm_w4(dev(A[idx]), wqd, wsd)), ref[idx], f"gemm_w4 M={M}")
