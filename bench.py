@@ -117,6 +117,19 @@ def copy_ceiling_gbs(torch):
     return 2.0 * n * 2 / t / 1e6
 
 
+def measured_ceilings(torch):
+    """What plain kernels sustain on this device, next to the published peaks: a streaming
+    read of 4 GiB (16-byte loads, 16 per thread in flight, 16384 work-groups; far larger
+    than the 256 MB Infinity Cache) and a bf16 MFMA loop with N(0, 1)
+    operands (1024 work-groups x 4 waves, 16 independent accumulators per wave), with the
+    shader clock its wave 0 counted (libbi_ceiling.so)."""
+    from invariant_deterministic_amd import ceiling
+    rate = ceiling.mfma_bf16_rate(torch)
+    return {"stream_read_gbs": ceiling.stream_read_gbs(torch), "mfma_bf16_tflops": rate["tflops"],
+            "mfma_clock_ghz": rate["clock_ghz"],
+            "probes": "streaming read of 4 GiB; v_mfma_f32_32x32x16_bf16 loop, bf16 N(0,1) operands"}
+
+
 def cpu_cores():
     try:
         return len(os.sched_getaffinity(0))
@@ -249,8 +262,12 @@ def run_mixed(args, torch, bi, synth):
     roof["traffic"] = recorded_traffic(roof)
     roof["kernel_ms"] = t_dec if roof["bound"] == "hbm" else t_gu
     copy_gbs = copy_ceiling_gbs(torch)
+    ceil = measured_ceilings(torch)
     if roof["bound"] == "hbm":
         roof["frac_of_torch_copy"] = roof["achieved"] / copy_gbs
+        roof["frac_of_stream_read"] = roof["achieved"] / ceil["stream_read_gbs"]
+    else:
+        roof["frac_of_mfma_sustained"] = roof["achieved"] / ceil["mfma_bf16_tflops"]
 
     out = {
         "metric": "batch-invariant block tokens/s",
@@ -258,7 +275,7 @@ def run_mixed(args, torch, bi, synth):
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "per_step_ms": per_step, "torch_copy_gbs": copy_gbs,
+        "per_step_ms": per_step, "torch_copy_gbs": copy_gbs, "ceilings": ceil,
         "dtype": "bf16 activations, int4 weights, fp32 accumulation", "data": "synthetic (seeded)",
         "config": {"workload": "int4 block hidden 4096, FFN 12288, 32/8 heads x 128: mixed step of "
                                f"{args.batch} decodes (KV 512..8192) + one 2048-token prefill chunk",
@@ -329,9 +346,12 @@ def run_gemm(args, torch, bi, synth):
         by = 2.0 * (M * K + N * K + M * N)
         res[M] = {"ms": t, "tflops": fl / t / 1e9, "gbs": by / t / 1e6,
                   "frac": max(fl / PEAK_BF16, by / PEAK_HBM) / (t * 1e-3)}
+    ceil = measured_ceilings(torch)
+    for r in res.values():
+        r["frac_of_mfma_sustained"] = r["tflops"] / ceil["mfma_bf16_tflops"]
     return {"metric": "bf16 GEMM K=N=4096 (no split-K, one tile)", "value": res[4096]["tflops"],
             "unit": "TFLOP/s", "config": {"workload": "C = A W^T, K = N = 4096, M in 1,7,64,513,4096"},
-            "per_m": res, "build_id": bi.build_id()}
+            "per_m": res, "ceilings": ceil, "build_id": bi.build_id()}
 
 
 def run_decode(args, torch, bi, synth):
