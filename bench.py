@@ -119,7 +119,7 @@ def copy_ceiling_gbs(torch):
 
 def measured_ceilings(torch):
     """What plain kernels sustain on this device, next to the published peaks: a streaming
-    read of 4 GiB (16-byte loads, 16 per thread in flight, 16384 work-groups; far larger
+    read of 4 GiB (16-byte non-temporal loads, 16 per thread in flight, 16384 work-groups; far larger
     than the 256 MB Infinity Cache) and a bf16 MFMA loop with N(0, 1)
     operands (1024 work-groups x 4 waves, 16 independent accumulators per wave), with the
     shader clock its wave 0 counted (libbi_ceiling.so)."""

@@ -7,7 +7,8 @@
  * benchmark, what a plain kernel sustains against the two limits the
  * batch-invariant kernels are priced against:
  *  - bic_stream_read: device-memory read bandwidth of a streaming kernel
- *    (16-byte loads, every byte read once, one word written per work-group);
+ *    (16-byte non-temporal loads, every byte read once, one word written per
+ *    work-group);
  *  - bic_mfma_bf16: the dense bf16 matrix-core rate with data-dependent
  *    operands (v_mfma_f32_32x32x16_bf16, 16 independent accumulators per wave,
  *    operands read once from device memory), and the shader clock while it runs.
