@@ -38,7 +38,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="mixed",
-                   choices=["mixed", "dense", "gemm", "decode", "norm", "tiny", "copy", "lmhead", "decode_q8"])
+                   choices=["mixed", "dense", "gemm", "decode", "norm", "tiny", "copy", "lmhead", "decode_q8",
+                            "ceilings"])
     p.add_argument("--batch", type=int, default=256, help="decode requests in the mixed step")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--kernel-reps", type=int, default=10)
@@ -564,6 +565,13 @@ def run_copy(args, torch, bi, synth):
             "bytes_read": n * 2, "bytes_written": n * 2, "config": {"workload": "1 GiB bf16 copy"}}
 
 
+def run_ceilings(args, torch, bi, synth):
+    """The two measurement probes alone (libbi_ceiling.so), for their own profiles."""
+    c = measured_ceilings(torch)
+    return {"metric": "measured ceilings", "value": c["stream_read_gbs"], "unit": "GB/s", **c,
+            "config": {"workload": "streaming read of 4 GiB; bf16 MFMA loop, 1024 x 4 waves x 20000 rounds"}}
+
+
 def main():
     global WARM_MS
     args = parse()
@@ -580,7 +588,7 @@ def main():
     bi.lib()
     fn = {"mixed": run_mixed, "dense": run_dense, "gemm": run_gemm, "decode": run_decode,
           "norm": run_norm, "tiny": run_tiny, "copy": run_copy, "lmhead": run_lmhead,
-          "decode_q8": run_decode_q8}[args.config]
+          "decode_q8": run_decode_q8, "ceilings": run_ceilings}[args.config]
     out = fn(args, torch, bi, synth)
     print(json.dumps(out), flush=True)
 
