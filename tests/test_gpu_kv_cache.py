@@ -136,3 +136,77 @@ def test_decode_paged_q8():
         one = bits(bi.attn_decode_paged_q8(dev(q_last[b:b + 1]), pool, tbl[b:b + 1], ld[b:b + 1], int(lens[b]), hq,
                                            scale))
         assert_bitwise(one[0], dec[b], f"request {b} alone")
+
+
+def test_decode_paged_q8_bench_workload():
+    """The int8 paged decode at the size and launch bench.py times: 256 requests with KV
+    lengths 513..8193, 32/8 heads x 128, 64-token pages in random order, requests longest
+    first.  Every request is bitwise equal to the bf16 prefill-order decode over the same cache
+    de-quantised (bf16(float(code) * scale)) and laid out contiguously, and to the same launch
+    without the order; sampled requests equal their run alone, their codes and scales equal the
+    oracle's quantisation of the same seeded rows, and their outputs are within tolerance of the
+    oracle's attention."""
+    device()
+    hq, hkv, d, B = 32, 8, 128, 256
+    lens = synth.uniform_ints(501, B, 512, 8192) + 1
+    npg = (lens + PAGE - 1) // PAGE
+    total = int(npg.sum())
+    perm = np.random.default_rng(1400).permutation(total).astype(np.int32)
+    tables = np.zeros((B, int(npg.max())), np.int32)
+    used, rows = 0, []
+    for b in range(B):
+        tables[b, :npg[b]] = perm[used:used + npg[b]]
+        used += int(npg[b])
+        rows.append(tables[b, np.arange(lens[b]) // PAGE].astype(np.int64) * PAGE + np.arange(lens[b]) % PAGE)
+    rows_np = np.concatenate(rows)
+    rows_d = torch.from_numpy(rows_np).cuda()
+    n = rows_np.size
+    CH = 1 << 18   # the seeded rows come in chunks of CH, each drawn on the device
+    pool = bi.KvPoolQ8(total, hkv, d)
+    for s0 in range(0, n, CH):
+        m = min(n - s0, CH)
+        bi.kv_append_q8(pool, synth.normal_bf16_device(1401 + s0, (m, hkv, d)),
+                        synth.normal_bf16_device(1402 + s0, (m, hkv, d)), rows_d[s0:s0 + m].contiguous())
+    q_host = synth.normal_bf16(402, (B, hq * d))
+    q = dev(q_host)
+    tbl = torch.from_numpy(tables).cuda()
+    ld = torch.from_numpy(lens.astype(np.int32)).cuda()
+    order = torch.from_numpy(np.argsort(-lens, kind="stable").astype(np.int32)).cuda()
+    mx, scale = int(lens.max()), 1.0 / math.sqrt(d)
+    announce("decode paged q8, bench workload: 256 requests, KV 513..8193")
+    dec = bits(bi.attn_decode_paged_q8(q, pool, tbl, ld, mx, hq, scale, order=order))
+    assert_bitwise(bits(bi.attn_decode_paged_q8(q, pool, tbl, ld, mx, hq, scale)), dec, "without the launch order")
+    # the de-quantised cache, contiguous in request order, through the bf16 prefill-order decode
+    offs = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+
+    def dequant(codes, sc):
+        return (codes[rows_d].float() * sc[rows_d].unsqueeze(-1)).to(torch.bfloat16)
+
+    kdq, vdq = dequant(pool.k, pool.ks), dequant(pool.v, pool.vs)
+    ref = bits(bi.attn_decode_prefill_order(q, kdq, vdq, torch.from_numpy(offs).cuda(), ld, mx, hq, hkv, d, scale,
+                                            order=order))
+    assert_bitwise(dec, ref, "paged q8 vs bf16 prefill-order decode on the de-quantised cache")
+    del kdq, vdq, ref
+
+    def seeded_rows(seed0, lo, hi):
+        """Rows lo..hi-1 of the seeded stream (chunks of CH rows drawn with seed seed0 + chunk start)."""
+        parts = []
+        for s0 in range(lo // CH * CH, hi, CH):
+            m = min(n - s0, CH)
+            parts.append(bits(synth.normal_bf16_device(seed0 + s0, (m, hkv, d))[max(lo, s0) - s0:min(hi, s0 + m) - s0]))
+        return np.concatenate(parts)
+
+    for b in (int(np.argmax(lens)), int(np.argmin(lens)), 17, 200):
+        announce("decode paged q8, bench workload, request", b, "L =", int(lens[b]))
+        one = bits(bi.attn_decode_paged_q8(q[b:b + 1], pool, tbl[b:b + 1], ld[b:b + 1], int(lens[b]), hq, scale))
+        assert_bitwise(one[0], dec[b], f"request {b} alone")
+        lo, hi = int(offs[b]), int(offs[b] + lens[b])
+        rb = torch.from_numpy(rows_np[lo:hi]).cuda()
+        kq, ks = KV.quantize(seeded_rows(1401, lo, hi))
+        vq, vs = KV.quantize(seeded_rows(1402, lo, hi))
+        assert np.array_equal(kq, pool.k[rb].cpu().numpy()) and np.array_equal(vq, pool.v[rb].cpu().numpy())
+        assert np.array_equal(ks.view(np.uint32), pool.ks[rb].cpu().numpy().view(np.uint32))
+        assert np.array_equal(vs.view(np.uint32), pool.vs[rb].cpu().numpy().view(np.uint32))
+        att = oracle.decode_attention(q_host[b].reshape(hq, d), KV.dequantize(kq, ks), KV.dequantize(vq, vs),
+                                      np.float32(scale))
+        assert_within_tolerance(dec[b], att.reshape(-1), f"request {b} parity")
