@@ -138,6 +138,17 @@ def cpu_cores():
         return os.cpu_count() or 1
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -326,10 +337,15 @@ def cpu_baseline_mixed(W, bi, torch):
     t0 = time.perf_counter()
     oracle.block_forward(cfg, W["w_host"], x, seqs, kpool, vpool)
     dt = time.perf_counter() - t0
+    # the sample's algorithmic flops: the block's linear layers for every token, causal prefill
+    # attention, and 4 D Hq flops per cached key of each decode request
+    H, F, hq, hkv, d = W["H"], W["F"], W["hq"], W["hkv"], W["d"]
+    lin = 2.0 * (nd + T) * (H * (hq + 2 * hkv) * d + hq * d * H + H * 2 * F + F * H)
+    att = 4.0 * d * hq * (T * (T + 1) / 2.0 + sum(float(L) + 1.0 for L in W["lens"][:nd]))
     return {"value": (nd + T) / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"{nd} decode requests (KV {min(W['lens'][:nd])}..{max(W['lens'][:nd])}) + one "
                       f"{T}-token prefill chunk of the same block, fp64 numpy, {dt:.1f} s",
-            "host_cores": cpu_cores()}
+            "gflops_fp64": (lin + att) / dt / 1e9, "host_cores": cpu_cores(), "cpu_model": cpu_model()}
 
 
 # --------------------------------------------- auxiliary workloads (profiling)
